@@ -1,0 +1,154 @@
+/*
+ * tgemm -- layout-aware bf16 GEMM for MI355X (gfx950) with fused epilogues.
+ *
+ * One C-ABI library.  Plain pointers and sizes only; every data pointer is a
+ * DEVICE pointer owned by the caller, and every call is asynchronous on the
+ * caller's HIP stream.
+ *
+ * What is computed
+ * ----------------
+ *   Y = op(A) . op(B),  op(X) = X for 'N' and X^T for 'T'.
+ *
+ *   The transpose is a flag, never a copy: a weight stored [N,K] row-major is
+ *   read in place as op(B) with transB = 'T' ("Strength reduction: fold
+ *   transpose into a subsequent GEMM call", the trace and its discussion of
+ *   NT GEMMs; the pitch asks for GEMMs that take transpose arguments).
+ *
+ * Storage convention (row-major, leading dimension = row stride in elements)
+ *   A 'N': [M,K], element (m,k) at A[m*lda + k]     lda >= K
+ *   A 'T': [K,M], element (m,k) at A[k*lda + m]     lda >= M
+ *   B 'N': [K,N], element (k,n) at B[k*ldb + n]     ldb >= N
+ *   B 'T': [N,K], element (k,n) at B[n*ldb + k]     ldb >= K
+ *   C    : [M,N], element (m,n) at C[m*ldc + n]     ldc >= N (>= 2N for ROPE)
+ *
+ * Epilogues (argument `epilogue`)
+ *   TGEMM_EPI_STORE_BF16   A, B bf16 -> C bf16, fp32 accumulation, output
+ *                          rounded to nearest even.
+ *   TGEMM_EPI_STORE_F32    A, B bf16 -> C fp32 (the raw accumulator).
+ *   TGEMM_EPI_CE           A, B bf16; the logits y = op(A).op(B) (fp32) are
+ *                          reduced per row and never written out:
+ *                            loss[m] = logsumexp_n y[m,n] - y[m, labels[m]]
+ *                          written to out_loss (fp32[M]).  If out_grad is not
+ *                          NULL it receives softmax(y) - onehot(labels) as
+ *                          bf16 [M,N] with row stride ldc.  C is ignored.
+ *                          ("Allow reductions in matmul epilogues": the
+ *                          attempted fusion defines the max / exp / sum / log
+ *                          steps, the loss and the softmax-minus-one-hot
+ *                          output; its answer on tile-wise row reductions
+ *                          describes the cross-tile combine.)
+ *                          Labels outside [0,N) are not checked on the host:
+ *                          that row's loss is NaN and its gradient row is the
+ *                          plain softmax.  No mean over rows, no scaling.
+ *   TGEMM_EPI_OUTER_F32    K must be 1.  A, B fp32; C fp32 [M,N] = the exact
+ *                          fp32 products a[m]*b[n].
+ *   TGEMM_EPI_ROPE_COSSIN  K must be 1.  A int64 positions (cast to fp32 in
+ *                          the kernel; exact for |p| < 2^24), B fp32 inverse
+ *                          frequencies.  t = fp32(a[m]) * b[n];
+ *                          C        = cos(t) as bf16 at columns n and n+N,
+ *                          out_grad = sin(t) as bf16 at columns n and n+N,
+ *                          both [M, 2N] with row stride ldc.
+ *                          ("Schedule a small matmul op as a reduction (or
+ *                          pointwise) op": the %kernel_math listing's K=1
+ *                          matmul, permute, duplicating cat and cos/cast, and
+ *                          the proposed broadcast-multiply decomposition.)
+ *
+ *   Any call with K == 1 and a STORE epilogue runs as a pointwise outer
+ *   product (no matrix cores), as that page proposes for K=1 matmuls.
+ *
+ * Errors
+ *   Arguments are validated before anything is enqueued; on any error
+ *   nothing is written.  No exceptions cross the ABI.  The call returns
+ *   after enqueueing and never synchronises; faults inside a kernel surface
+ *   at the caller's next synchronisation.  Outputs must not alias inputs.
+ *
+ * Workspace
+ *   TGEMM_EPI_CE needs a small scratch buffer (per row and per 128-column
+ *   block: the block max and block sum of exponentials, plus per row the
+ *   label logit and the logsumexp).  It is allocated stream-ordered
+ *   (hipMallocAsync / hipFreeAsync on `stream`), so calls on different
+ *   streams do not share it.
+ */
+#ifndef TGEMM_H
+#define TGEMM_H
+
+#include <stdint.h>
+
+#if defined(__GNUC__) || defined(__clang__)
+#define TGEMM_API __attribute__((visibility("default")))
+#else
+#define TGEMM_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  TGEMM_OK = 0,
+  TGEMM_ERR_INVALID_ARG = -1, /* a flag, size, leading dimension or pointer is invalid */
+  TGEMM_ERR_UNSUPPORTED = -2, /* valid request this library does not implement      */
+  TGEMM_ERR_HIP = -3,         /* the HIP runtime reported an error while enqueueing   */
+  TGEMM_ERR_NO_MEMORY = -4    /* the CE workspace could not be allocated              */
+} tgemm_status;
+
+typedef enum {
+  TGEMM_EPI_STORE_BF16 = 0,
+  TGEMM_EPI_STORE_F32 = 1,
+  TGEMM_EPI_CE = 2,
+  TGEMM_EPI_OUTER_F32 = 3,
+  TGEMM_EPI_ROPE_COSSIN = 4
+} tgemm_epilogue;
+
+/*
+ * Run one GEMM with the chosen epilogue on `stream` (a hipStream_t; NULL is
+ * the null stream).
+ *
+ *   transA, transB  'N'/'n' or 'T'/'t' (see the storage convention above).
+ *   M, N, K         >= 1 and < 2^31.
+ *   A, lda          operand A (bf16; fp32 for OUTER_F32; int64 for ROPE).
+ *   B, ldb          operand B (bf16; fp32 for OUTER_F32 and ROPE).
+ *   C, ldc          output (bf16 or fp32; cos table for ROPE; unused by CE).
+ *                   For CE, ldc is the row stride of out_grad.
+ *   labels          CE only: int32[M].
+ *   out_loss        CE only: fp32[M].
+ *   out_grad        CE: optional bf16 [M,N] (row stride ldc);
+ *                   ROPE: required sin table bf16 [M,2N] (row stride ldc).
+ *
+ * Returns TGEMM_OK or a negative tgemm_status.
+ */
+TGEMM_API int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t K,
+              const void* A, int64_t lda, const void* B, int64_t ldb,
+              void* C, int64_t ldc, int epilogue,
+              const int32_t* labels, float* out_loss, void* out_grad,
+              void* stream);
+
+/*
+ * Host-only argument check with the same rules as tgemm_run, without
+ * touching the GPU.  Returns TGEMM_OK or the status tgemm_run would return.
+ */
+TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                   const void* A, int64_t lda, const void* B, int64_t ldb,
+                   const void* C, int64_t ldc, int epilogue,
+                   const int32_t* labels, const float* out_loss,
+                   const void* out_grad);
+
+/* Human-readable name of a status code (static string, never NULL). */
+TGEMM_API const char* tgemm_status_string(int status);
+
+/*
+ * Tuning / testing knob: force the GEMM tile configuration for subsequent
+ * calls from this process.  0 = automatic (default); 1 = 256x256 tiles;
+ * 2 = 128x128 tiles.  Returns the previous value, or
+ * TGEMM_ERR_INVALID_ARG for an unknown value.
+ * Not thread-safe with concurrent tgemm_run calls.
+ */
+TGEMM_API int tgemm_set_tile_config(int config);
+
+/* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
+TGEMM_API int tgemm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TGEMM_H */

@@ -1,0 +1,121 @@
+// Cross-entropy combine and gradient fix-up kernels.
+//
+// "Allow reductions in matmul epilogues" asks whether a row-wise reduction
+// can run when the matmul is computed tile by tile; the answer given there
+// is a grid reduction (atomics or semaphores), and a cooperative launch
+// when the reduced value feeds back into other epilogue outputs.  Here the
+// GEMM epilogue leaves one (block max, block sum) pair per row and per
+// column block; `ce_combine` folds those pairs per row in ascending block
+// order (a fixed order, so the result is deterministic), and the gradient,
+// which needs the row's final logsumexp, is finished by `ce_grad_fixup`
+// in a second pass instead of a cooperative launch.
+#include "tgemm_internal.h"
+
+namespace tgemm {
+
+namespace {
+
+constexpr float kLog2eF = 1.4426950408889634f;
+constexpr float kLn2F = 0.6931471805599453f;
+
+__device__ __forceinline__ float exp_f(float x) { return exp2f(x * kLog2eF); }
+
+__device__ __forceinline__ uint32_t f2bf_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// One thread per row.  (m, s) (+) (m', s') = (max, s e^{m-max} + s' e^{m'-max});
+// a pair with s == 0 is the identity (-inf, 0) and is skipped.
+__global__ void __launch_bounds__(256) ce_combine_kernel(
+    const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ ylab,
+    const int32_t* __restrict__ labels, int M, int N, int nblk, float* __restrict__ loss,
+    float* __restrict__ lse_out) {
+  const int row = blockIdx.x * blockDim.x + threadIdx.x;
+  if (row >= M) return;
+  float m = -INFINITY, s = 0.f;
+  for (int t = 0; t < nblk; ++t) {
+    const float mt = pm[(int64_t)t * M + row];
+    const float st = ps[(int64_t)t * M + row];
+    if (!(st > 0.f)) continue;
+    if (s > 0.f) {
+      const float mx = fmaxf(m, mt);
+      s = s * exp_f(m - mx) + st * exp_f(mt - mx);
+      m = mx;
+    } else {
+      m = mt;
+      s = st;
+    }
+  }
+  const float lse = m + log2f(s) * kLn2F;
+  const int lab = labels[row];
+  loss[row] = (lab >= 0 && lab < N) ? lse - ylab[row] : __int_as_float(0x7fc00000);
+  lse_out[row] = lse;
+}
+
+// grad[r, c] currently holds bf16(exp(y - m_blk)); rescale by
+// exp(m_blk - lse) and subtract the one-hot term.  Each thread handles 8
+// consecutive columns of one row (one 16-byte vector when aligned).
+__global__ void __launch_bounds__(256) ce_grad_fixup_kernel(
+    uint16_t* __restrict__ grad, int64_t ldc, const float* __restrict__ pm,
+    const float* __restrict__ lse, const int32_t* __restrict__ labels, int M, int N,
+    int blk_cols, int vec_ok) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int groups = (N + 7) >> 3;
+  const int64_t row64 = gid / groups;
+  if (row64 >= M) return;
+  const int row = (int)row64;
+  const int c0 = (int)(gid - row64 * groups) * 8;
+  const float l = lse[row];
+  const int lab = labels[row];
+  uint16_t* g = grad + row64 * ldc + c0;
+  if (vec_ok && c0 + 8 <= N && (c0 / blk_cols) == ((c0 + 7) / blk_cols)) {
+    const float scale = exp_f(pm[(int64_t)(c0 / blk_cols) * M + row] - l);
+    uint4 v = *reinterpret_cast<const uint4*>(g);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int c = c0 + 2 * q;
+      float lo = bf2f(w[q] & 0xffffu) * scale - (c == lab ? 1.f : 0.f);
+      float hi = bf2f(w[q] >> 16) * scale - (c + 1 == lab ? 1.f : 0.f);
+      w[q] = f2bf_rne(lo) | (f2bf_rne(hi) << 16);
+    }
+    *reinterpret_cast<uint4*>(g) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else {
+    for (int e = 0; e < 8 && c0 + e < N; ++e) {
+      const int c = c0 + e;
+      const float scale = exp_f(pm[(int64_t)(c / blk_cols) * M + row] - l);
+      const float v = bf2f(g[e]) * scale - (c == lab ? 1.f : 0.f);
+      g[e] = (uint16_t)f2bf_rne(v);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ce_combine(const float* part_m, const float* part_s, const float* ylabel,
+                             const int32_t* labels, int M, int N, int nblk, float* loss,
+                             float* lse, hipStream_t s) {
+  const int blocks = (M + 255) / 256;
+  hipLaunchKernelGGL(ce_combine_kernel, dim3(blocks), dim3(256), 0, s, part_m, part_s, ylabel,
+                     labels, M, N, nblk, loss, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_ce_grad_fixup(uint16_t* grad, int64_t ldc, const float* part_m,
+                                const float* lse, const int32_t* labels, int M, int N,
+                                int blk_cols, hipStream_t s) {
+  const int groups = (N + 7) / 8;
+  const int64_t threads = (int64_t)M * groups;
+  const int64_t blocks = (threads + 255) / 256;
+  const int vec_ok = ((reinterpret_cast<uintptr_t>(grad) & 15) == 0) && (ldc % 8 == 0);
+  hipLaunchKernelGGL(ce_grad_fixup_kernel, dim3((unsigned)blocks), dim3(256), 0, s, grad, ldc,
+                     part_m, lse, labels, M, N, blk_cols, vec_ok);
+  return hipGetLastError();
+}
+
+}  // namespace tgemm

@@ -1,0 +1,147 @@
+// tgemm_run: validation, path selection, tile choice, workspace and launch.
+#include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+
+#include "tgemm.h"
+#include "tgemm_internal.h"
+
+namespace tgemm {
+namespace {
+
+int g_forced_tile = kTileAuto;
+
+inline bool is_n(char t) { return t == 'N' || t == 'n'; }
+
+inline int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+// A dispatch packet's grid is at most 2^32 - 1 work-items.
+constexpr int64_t kMaxWorkgroups = (int64_t(1) << 24) - 1;
+
+bool verbose() {
+  static int v = -1;
+  if (v < 0) {
+    const char* e = getenv("TGEMM_VERBOSE");
+    v = (e && e[0] && e[0] != '0') ? 1 : 0;
+  }
+  return v == 1;
+}
+
+// Tile choice: 256x256 tiles when they alone give at least one tile per
+// compute unit (256 CUs), else 128x128 tiles for more parallelism.
+int choose_tile(int M, int N) {
+  if (g_forced_tile != kTileAuto) return g_forced_tile;
+  const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+  return t256 >= 240 ? kTile256 : kTile128;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP; }
+
+hipError_t launch_gemm(char ta, char tb, int cfg, int epi, const GemmParams& p, hipStream_t s) {
+  const bool an = is_n(ta), bn = is_n(tb);
+  if (an && bn) return launch_gemm_nn(cfg, epi, p, s);
+  if (an && !bn) return launch_gemm_nt(cfg, epi, p, s);
+  if (!an && bn) return launch_gemm_tn(cfg, epi, p, s);
+  return launch_gemm_tt(cfg, epi, p, s);
+}
+
+}  // namespace
+}  // namespace tgemm
+
+using namespace tgemm;
+
+extern "C" int tgemm_set_tile_config(int config) {
+  if (config < kTileAuto || config > kTile128) return TGEMM_ERR_INVALID_ARG;
+  const int prev = g_forced_tile;
+  g_forced_tile = config;
+  return prev;
+}
+
+extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                         int64_t ldc, int epilogue, const int32_t* labels, float* out_loss,
+                         void* out_grad, void* stream) {
+  const int st = tgemm_validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
+                                out_loss, out_grad);
+  if (st != TGEMM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int m = (int)M, n = (int)N, k = (int)K;
+
+  // Element strides of the length-M / length-N vectors of a K=1 product.
+  const int64_t sa = is_n(transA) ? lda : 1;
+  const int64_t sb = is_n(transB) ? 1 : ldb;
+
+  if (epilogue == TGEMM_EPI_ROPE_COSSIN || epilogue == TGEMM_EPI_OUTER_F32 ||
+      (K == 1 && (epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32))) {
+    const int64_t groups = epilogue == TGEMM_EPI_ROPE_COSSIN ? (N + 7) / 8 : (N + 3) / 4;
+    if ((M * groups + 255) / 256 > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
+    if (verbose()) fprintf(stderr, "tgemm: K=1 pointwise path, epilogue %d\n", epilogue);
+    hipError_t e;
+    if (epilogue == TGEMM_EPI_ROPE_COSSIN)
+      e = launch_k1_rope(static_cast<const int64_t*>(A), sa, static_cast<const float*>(B), sb, m,
+                         n, static_cast<uint16_t*>(C), static_cast<uint16_t*>(out_grad), ldc, s);
+    else if (epilogue == TGEMM_EPI_OUTER_F32)
+      e = launch_k1_outer_f32(static_cast<const float*>(A), sa, static_cast<const float*>(B), sb,
+                              m, n, static_cast<float*>(C), ldc, s);
+    else
+      e = launch_k1_outer_bf16(static_cast<const uint16_t*>(A), sa,
+                               static_cast<const uint16_t*>(B), sb, m, n, C, ldc,
+                               epilogue == TGEMM_EPI_STORE_F32, s);
+    return status_of(e);
+  }
+
+  const int cfg = choose_tile(m, n);
+  GemmParams p = {};
+  p.A = static_cast<const uint16_t*>(A);
+  p.B = static_cast<const uint16_t*>(B);
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = m;
+  p.N = n;
+  p.K = k;
+  p.tilesM = ceil_div(M, tile_rows(cfg));
+  p.tilesN = ceil_div(N, tile_cols(cfg));
+  if ((int64_t)p.tilesM * p.tilesN > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
+  p.groupM = p.tilesM < 4 ? p.tilesM : (p.tilesM <= 8 ? p.tilesM : 4);
+  p.aligned = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0 &&
+              lda % 8 == 0 && ldb % 8 == 0;
+  if (verbose())
+    fprintf(stderr, "tgemm: gemm %c%c M=%d N=%d K=%d tile=%d grid=%dx%d groupM=%d aligned=%d epi=%d\n",
+            transA, transB, m, n, k, cfg, p.tilesM, p.tilesN, p.groupM, p.aligned, epilogue);
+
+  if (epilogue != TGEMM_EPI_CE) {
+    p.C = C;
+    return status_of(launch_gemm(transA, transB, cfg,
+                                 epilogue == TGEMM_EPI_STORE_BF16 ? kEpiStoreBf16 : kEpiStoreF32,
+                                 p, s));
+  }
+
+  // Cross-entropy: GEMM + per-block partials, then the per-row combine,
+  // then (with a gradient) the rescale pass.
+  if (out_grad != nullptr && ((M * ((N + 7) / 8) + 255) / 256) > kMaxWorkgroups)
+    return TGEMM_ERR_UNSUPPORTED;
+  const int blk = ce_block_cols(cfg);
+  const int nblk = p.tilesN * (tile_cols(cfg) / blk);
+  const size_t ws_floats = 2 * (size_t)nblk * M + 2 * (size_t)M;
+  float* ws = nullptr;
+  if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_floats * sizeof(float), s) != hipSuccess ||
+      ws == nullptr) {
+    (void)hipGetLastError();
+    return TGEMM_ERR_NO_MEMORY;
+  }
+  p.labels = labels;
+  p.part_m = ws;
+  p.part_s = ws + (size_t)nblk * M;
+  p.ylabel = ws + 2 * (size_t)nblk * M;
+  float* lse = p.ylabel + M;
+  p.grad = static_cast<uint16_t*>(out_grad);
+  hipError_t e = launch_gemm(transA, transB, cfg, kEpiCE, p, s);
+  if (e == hipSuccess)
+    e = launch_ce_combine(p.part_m, p.part_s, p.ylabel, labels, m, n, nblk, out_loss, lse, s);
+  if (e == hipSuccess && out_grad != nullptr)
+    e = launch_ce_grad_fixup(p.grad, ldc, p.part_m, lse, labels, m, n, blk, s);
+  const hipError_t ef = hipFreeAsync(ws, s);
+  if (e == hipSuccess) e = ef;
+  return status_of(e);
+}

@@ -1,0 +1,143 @@
+// Degenerate K=1 matmuls as pointwise kernels (no matrix cores).
+//
+// "Schedule a small matmul op as a reduction (or pointwise) op": with K=1
+// the matmul is a broadcast of both operands, one elementwise multiply and
+// a squeeze, so it can live in the same kernel as the pointwise work around
+// it.  For the RoPE table the listing widens the [64] inverse frequencies
+// and casts the int64 positions to fp32, multiplies, permutes to
+// [positions, 64], duplicates the last dimension to 128 and takes cos (and,
+// for the second declared output, sin) before casting to bf16.  Here the
+// permute is free (positions are operand A, so the product is produced
+// directly as [positions, 64]; fp32 multiplication commutes exactly), the
+// duplication is a second store of the same value, and everything from the
+// int64 load to the bf16 stores is one kernel.
+#include "tgemm_internal.h"
+
+namespace tgemm {
+
+namespace {
+
+__device__ __forceinline__ uint32_t f2bf_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+
+// One thread per (row, group of 8 columns).
+__global__ void __launch_bounds__(256) k1_rope_kernel(
+    const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf, int64_t sinv,
+    int M, int N, uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out, int64_t ldc,
+    int vec_ok) {
+  const int groups = (N + 7) >> 3;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / groups;
+  if (row >= M) return;
+  const int c0 = (int)(gid - row * groups) * 8;
+  const float p = (float)pos[row * spos];  // int64 -> fp32 (exact below 2^24)
+  uint16_t* co = cos_out + row * ldc;
+  uint16_t* so = sin_out + row * ldc;
+  if (vec_ok && c0 + 8 <= N) {
+    const float4 f0 = *reinterpret_cast<const float4*>(invf + c0);
+    const float4 f1 = *reinterpret_cast<const float4*>(invf + c0 + 4);
+    const float fr[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    uint32_t cw[4], sw[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float s0, c0v, s1, c1v;
+      sincosf(__fmul_rn(p, fr[2 * q]), &s0, &c0v);
+      sincosf(__fmul_rn(p, fr[2 * q + 1]), &s1, &c1v);
+      cw[q] = f2bf_rne(c0v) | (f2bf_rne(c1v) << 16);
+      sw[q] = f2bf_rne(s0) | (f2bf_rne(s1) << 16);
+    }
+    const uint4 cv = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+    const uint4 sv = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+    *reinterpret_cast<uint4*>(co + c0) = cv;
+    *reinterpret_cast<uint4*>(co + c0 + N) = cv;
+    *reinterpret_cast<uint4*>(so + c0) = sv;
+    *reinterpret_cast<uint4*>(so + c0 + N) = sv;
+  } else {
+    for (int e = 0; e < 8 && c0 + e < N; ++e) {
+      const int c = c0 + e;
+      float sv, cv;
+      sincosf(__fmul_rn(p, invf[c * sinv]), &sv, &cv);
+      const uint16_t cb = (uint16_t)f2bf_rne(cv), sb = (uint16_t)f2bf_rne(sv);
+      co[c] = cb;
+      co[c + N] = cb;
+      so[c] = sb;
+      so[c + N] = sb;
+    }
+  }
+}
+
+// C[m, n] = a[m] * b[n], fp32 inputs, one fp32 multiply.
+__global__ void __launch_bounds__(256) k1_outer_f32_kernel(const float* __restrict__ a, int64_t sa,
+                                                           const float* __restrict__ b, int64_t sb,
+                                                           int M, int N, float* __restrict__ C,
+                                                           int64_t ldc) {
+  const int groups = (N + 3) >> 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / groups;
+  if (row >= M) return;
+  const int c0 = (int)(gid - row * groups) * 4;
+  const float av = a[row * sa];
+  float* out = C + row * ldc;
+  for (int e = 0; e < 4 && c0 + e < N; ++e) out[c0 + e] = __fmul_rn(av, b[(int64_t)(c0 + e) * sb]);
+}
+
+// K = 1 with bf16 operands and a store epilogue: the bf16 x bf16 product is
+// exact in fp32, then stored as fp32 or rounded to bf16.
+__global__ void __launch_bounds__(256) k1_outer_bf16_kernel(
+    const uint16_t* __restrict__ a, int64_t sa, const uint16_t* __restrict__ b, int64_t sb, int M,
+    int N, void* __restrict__ C, int64_t ldc, int out_f32) {
+  const int groups = (N + 3) >> 2;
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  const int64_t row = gid / groups;
+  if (row >= M) return;
+  const int c0 = (int)(gid - row * groups) * 4;
+  const float av = bf2f(a[row * sa]);
+  for (int e = 0; e < 4 && c0 + e < N; ++e) {
+    const float v = __fmul_rn(av, bf2f(b[(int64_t)(c0 + e) * sb]));
+    if (out_f32)
+      reinterpret_cast<float*>(C)[row * ldc + c0 + e] = v;
+    else
+      reinterpret_cast<uint16_t*>(C)[row * ldc + c0 + e] = (uint16_t)f2bf_rne(v);
+  }
+}
+
+inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_k1_rope(const int64_t* pos, int64_t spos, const float* invf, int64_t sinv,
+                          int M, int N, uint16_t* cos_out, uint16_t* sin_out, int64_t ldc,
+                          hipStream_t s) {
+  const int vec_ok = sinv == 1 && (reinterpret_cast<uintptr_t>(invf) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(cos_out) & 15) == 0 &&
+                     (reinterpret_cast<uintptr_t>(sin_out) & 15) == 0 && ldc % 8 == 0 &&
+                     N % 8 == 0;
+  const int64_t threads = (int64_t)M * ((N + 7) / 8);
+  hipLaunchKernelGGL(k1_rope_kernel, dim3(grid_for(threads)), dim3(256), 0, s, pos, spos, invf,
+                     sinv, M, N, cos_out, sin_out, ldc, vec_ok);
+  return hipGetLastError();
+}
+
+hipError_t launch_k1_outer_f32(const float* a, int64_t sa, const float* b, int64_t sb, int M,
+                               int N, float* C, int64_t ldc, hipStream_t s) {
+  const int64_t threads = (int64_t)M * ((N + 3) / 4);
+  hipLaunchKernelGGL(k1_outer_f32_kernel, dim3(grid_for(threads)), dim3(256), 0, s, a, sa, b, sb,
+                     M, N, C, ldc);
+  return hipGetLastError();
+}
+
+hipError_t launch_k1_outer_bf16(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb,
+                                int M, int N, void* C, int64_t ldc, bool out_f32, hipStream_t s) {
+  const int64_t threads = (int64_t)M * ((N + 3) / 4);
+  hipLaunchKernelGGL(k1_outer_bf16_kernel, dim3(grid_for(threads)), dim3(256), 0, s, a, sa, b, sb,
+                     M, N, C, ldc, out_f32 ? 1 : 0);
+  return hipGetLastError();
+}
+
+}  // namespace tgemm

@@ -1,0 +1,63 @@
+// Internal declarations shared by the host dispatcher and the kernel
+// translation units.  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tgemm {
+
+// Epilogue variants of the matrix-core GEMM kernel.
+enum EpiKind : int { kEpiStoreBf16 = 0, kEpiStoreF32 = 1, kEpiCE = 2 };
+
+// Tile configurations of the GEMM kernel (workgroup tile BM x BN, 4 waves in
+// a 2x2 arrangement, k-step 64).
+enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2 };
+
+struct GemmParams {
+  const uint16_t* A;  // bf16 bits
+  const uint16_t* B;  // bf16 bits
+  int64_t lda, ldb, ldc;
+  int M, N, K;
+  int tilesM, tilesN, groupM;
+  int aligned;        // A, B 16-byte aligned and lda, ldb multiples of 8
+  void* C;            // store epilogues
+  // cross-entropy epilogue
+  const int32_t* labels;
+  float* part_m;      // [nColBlocks][M] block max
+  float* part_s;      // [nColBlocks][M] block sum of exp(y - block max)
+  float* ylabel;      // [M] logit at the label column
+  uint16_t* grad;     // optional [M][ldc] bf16: exp(y - block max), fixed up later
+};
+
+// Width (in columns) of the per-row partial blocks the CE epilogue writes.
+inline int ce_block_cols(int cfg) { return cfg == kTile256 ? 128 : 64; }
+inline int tile_rows(int cfg) { return cfg == kTile256 ? 256 : 128; }
+inline int tile_cols(int cfg) { return cfg == kTile256 ? 256 : 128; }
+
+// One launcher per operand layout (defined in gemm_<layout>.hip).
+hipError_t launch_gemm_nn(int cfg, int epi, const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_nt(int cfg, int epi, const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_tn(int cfg, int epi, const GemmParams& p, hipStream_t s);
+hipError_t launch_gemm_tt(int cfg, int epi, const GemmParams& p, hipStream_t s);
+
+// Cross-entropy combine (per row: fold block partials in ascending block
+// order, loss = lse - y[label]) and gradient fix-up (defined in ce.hip).
+hipError_t launch_ce_combine(const float* part_m, const float* part_s, const float* ylabel,
+                             const int32_t* labels, int M, int N, int nblk, float* loss,
+                             float* lse, hipStream_t s);
+hipError_t launch_ce_grad_fixup(uint16_t* grad, int64_t ldc, const float* part_m,
+                                const float* lse, const int32_t* labels, int M, int N,
+                                int blk_cols, hipStream_t s);
+
+// K = 1 pointwise paths (defined in k1.hip).  Strides are element strides
+// of the length-M vector a and the length-N vector b.
+hipError_t launch_k1_rope(const int64_t* pos, int64_t spos, const float* invf, int64_t sinv,
+                          int M, int N, uint16_t* cos_out, uint16_t* sin_out, int64_t ldc,
+                          hipStream_t s);
+hipError_t launch_k1_outer_f32(const float* a, int64_t sa, const float* b, int64_t sb, int M,
+                               int N, float* C, int64_t ldc, hipStream_t s);
+hipError_t launch_k1_outer_bf16(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb,
+                                int M, int N, void* C, int64_t ldc, bool out_f32, hipStream_t s);
+
+}  // namespace tgemm

@@ -1,0 +1,142 @@
+"""GPU parity of the cross-entropy epilogue against the oracle (C-ABI calls)."""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from layout_aware_gemm_amd import tgemm
+from parity_util import (GEMM_BF16_TOL, LOSS_REL_TOL, bf16_to_f64, bits, dev, rel_err,
+                         sample_rows, scaled_err)
+
+pytestmark = pytest.mark.gpu
+
+
+def run_ce(A, lda, B, ldb, labels, M, N, K, ta="N", tb="T", grad=False, cfg=0, ldg=None):
+    loss = torch.full((M,), float("nan"), dtype=torch.float32, device=dev())
+    ldg = N if ldg is None else ldg
+    g = torch.full((M, ldg), float("nan"), dtype=torch.bfloat16, device=dev()) if grad else None
+    prev = tgemm.set_tile_config(cfg)
+    try:
+        tgemm.run(ta, tb, M, N, K, A, lda, B, ldb, None, ldg, tgemm.EPI_CE, labels=labels,
+                  out_loss=loss, out_grad=g)
+    finally:
+        tgemm.set_tile_config(prev)
+    torch.cuda.synchronize()
+    return loss, g
+
+
+def oracle_ce(d, ta, tb, M, N, K, labels, rows=None):
+    y = oracle.gemm(ta, tb, M, N, K, bits(d["A"]).reshape(-1), d["lda"],
+                    bits(d["B"]).reshape(-1), d["ldb"], rows=rows)
+    lab = labels.numpy() if rows is None else labels.numpy()[rows]
+    return oracle.cross_entropy(y, lab)
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_tiny_ce_config(cfg):
+    """A bf16[64,128], W bf16[256,128]; C as fp32, loss and grad."""
+    w = workloads.tiny_ce()
+    A, W, lab = w["A"].to(dev()), w["W"].to(dev()), w["labels"].to(dev())
+    d = {"A": w["A"], "lda": 128, "B": w["W"], "ldb": 128}
+    C = torch.empty(64, 256, dtype=torch.float32, device=dev())
+    tgemm.run("N", "T", 64, 256, 128, A, 128, W, 128, C, 256, tgemm.EPI_STORE_F32)
+    loss, g = run_ce(A, 128, W, 128, lab, 64, 256, 128, grad=True, cfg=cfg)
+    ref_loss, ref_grad, _ = oracle_ce(d, "N", "T", 64, 256, 128, w["labels"])
+    ref_c = oracle.gemm("N", "T", 64, 256, 128, bits(w["A"]).reshape(-1), 128,
+                        bits(w["W"]).reshape(-1), 128)
+    assert scaled_err(C.cpu().numpy(), ref_c) <= 1e-5        # fp32 output
+    assert rel_err(loss.cpu().numpy(), ref_loss) <= LOSS_REL_TOL
+    assert scaled_err(bf16_to_f64(g), ref_grad) <= GEMM_BF16_TOL
+    # grad rows sum to ~0 (two bf16 roundings per element: store, then rescale)
+    assert np.abs(bf16_to_f64(g).sum(axis=1)).max() <= 2.0 ** -7 + 1e-4
+
+
+LAYOUTS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 3, 7), (70, 300, 96), (257, 520, 130),
+                                   (300, 1000, 64), (129, 64, 1)])
+def test_ce_ragged(M, N, K, ta, tb, cfg):
+    d = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K, std=1.0, pad=1)
+    g = torch.Generator().manual_seed(M * N)
+    labels = torch.randint(0, N, (M,), generator=g, dtype=torch.int32)
+    loss, gr = run_ce(d["A"].to(dev()), d["lda"], d["B"].to(dev()), d["ldb"], labels.to(dev()),
+                      M, N, K, ta, tb, grad=True, cfg=cfg, ldg=N + 3)
+    ref_loss, ref_grad, _ = oracle_ce(d, ta, tb, M, N, K, labels)
+    l = loss.cpu().numpy()
+    if N == 1:
+        assert np.all(np.abs(l) <= 1e-6)
+    else:
+        assert rel_err(l, ref_loss) <= LOSS_REL_TOL
+    assert scaled_err(bf16_to_f64(gr[:, :N]), ref_grad) <= GEMM_BF16_TOL
+    assert torch.isnan(gr[:, N:].float()).all()
+
+
+def test_zero_logits_give_ln_n():
+    M, N, K = 64, 32000, 64
+    A = torch.zeros(M, K, dtype=torch.bfloat16, device=dev())
+    W = torch.randn(N, K, generator=torch.Generator().manual_seed(1)).to(torch.bfloat16).to(dev())
+    labels = torch.randint(0, N, (M,), generator=torch.Generator().manual_seed(2),
+                           dtype=torch.int32)
+    loss, g = run_ce(A, K, W, K, labels.to(dev()), M, N, K, grad=True)
+    assert np.abs(loss.cpu().numpy() - math.log(N)).max() <= 1e-3 * math.log(N)
+    gg = bf16_to_f64(g)
+    onehot = np.zeros((M, N))
+    onehot[np.arange(M), labels.numpy()] = 1
+    assert scaled_err(gg, 1.0 / N - onehot) <= GEMM_BF16_TOL
+
+
+def test_out_of_range_labels_give_nan():
+    M, N, K = 8, 300, 32
+    d = workloads.random_operands(M, N, K, "N", "T", seed=4)
+    labels = torch.tensor([0, 299, 300, -1, 5, 1 << 30, 7, 150], dtype=torch.int32)
+    loss, g = run_ce(d["A"].to(dev()), K, d["B"].to(dev()), K, labels.to(dev()), M, N, K,
+                     grad=True)
+    l = loss.cpu().numpy()
+    bad = np.array([False, False, True, True, False, True, False, False])
+    assert np.all(np.isnan(l[bad])) and np.all(np.isfinite(l[~bad]))
+    ref_loss, ref_grad, _ = oracle_ce(d, "N", "T", M, N, K, labels)
+    assert rel_err(l[~bad], ref_loss[~bad]) <= LOSS_REL_TOL
+    assert scaled_err(bf16_to_f64(g), ref_grad) <= GEMM_BF16_TOL
+
+
+def test_ce_deterministic_and_grad_mode_same_loss():
+    M, N, K = 512, 3000, 256
+    d = workloads.random_operands(M, N, K, "N", "T", seed=9)
+    labels = torch.randint(0, N, (M,), generator=torch.Generator().manual_seed(3),
+                           dtype=torch.int32).to(dev())
+    A, B = d["A"].to(dev()), d["B"].to(dev())
+    l0, _ = run_ce(A, K, B, K, labels, M, N, K)
+    for _ in range(5):
+        l1, _ = run_ce(A, K, B, K, labels, M, N, K)
+        assert torch.equal(l0, l1)
+    l2, _ = run_ce(A, K, B, K, labels, M, N, K, grad=True)
+    assert torch.equal(l0, l2)
+
+
+def test_ce_vocab_full_size():
+    """H bf16[4096,4096], W bf16[32000,4096], labels in [0,32000): loss-only
+    and loss+grad, sampled rows against the oracle."""
+    w = workloads.ce_vocab()
+    H, W, lab = w["H"].to(dev()), w["W"].to(dev()), w["labels"].to(dev())
+    M, N, K = 4096, 32000, 4096
+    loss = tgemm.cross_entropy(H, W.t(), lab)
+    loss2, g = tgemm.cross_entropy(H, W.t(), lab, grad=True)
+    torch.cuda.synchronize()
+    assert torch.equal(loss, loss2)
+    rows = sample_rows(M, 24, seed=4, tile=256)
+    d = {"A": w["H"], "lda": K, "B": w["W"], "ldb": K}
+    ref_loss, ref_grad, _ = oracle_ce(d, "N", "T", M, N, K, w["labels"], rows=rows)
+    r = torch.as_tensor(rows, device=dev())
+    assert rel_err(loss[r].cpu().numpy(), ref_loss) <= LOSS_REL_TOL
+    assert scaled_err(bf16_to_f64(g[r]), ref_grad) <= GEMM_BF16_TOL
+    # every row of the gradient sums to ~0 and every loss is positive
+    sums = g.float().sum(dim=1)
+    assert sums.abs().max().item() <= 2.0 ** -7 + 1e-3
+    assert (loss > 0).all().item()

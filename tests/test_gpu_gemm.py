@@ -1,0 +1,156 @@
+"""GPU parity of the layout-aware GEMM (store epilogues) against the oracle.
+
+Every call goes through the C-ABI (``tgemm.run``).  Inputs are seeded and
+identical on both sides; expected values come only from ``oracle``.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from layout_aware_gemm_amd import tgemm
+from parity_util import (GEMM_BF16_TOL, bf16_to_f64, bits, dev, oracle_gemm_from, sample_rows,
+                         scaled_err)
+
+pytestmark = pytest.mark.gpu
+
+LAYOUTS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
+RAGGED = [(1, 1, 1), (3, 7, 13), (33, 65, 257), (257, 129, 65), (300, 333, 200),
+          (129, 257, 1000), (64, 256, 128), (520, 136, 72)]
+
+
+def run_store(d, ta, tb, M, N, K, out_dtype=torch.bfloat16, cfg=0, ldc=None):
+    A = d["A"].to(dev())
+    B = d["B"].to(dev())
+    ldc = N if ldc is None else ldc
+    C = torch.full((M, ldc), float("nan"), dtype=out_dtype, device=dev())
+    epi = tgemm.EPI_STORE_BF16 if out_dtype == torch.bfloat16 else tgemm.EPI_STORE_F32
+    prev = tgemm.set_tile_config(cfg)
+    try:
+        tgemm.run(ta, tb, M, N, K, A, d["lda"], B, d["ldb"], C, ldc, epi)
+    finally:
+        tgemm.set_tile_config(prev)
+    torch.cuda.synchronize()
+    return C
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("pad", [0, 3])
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", RAGGED)
+def test_ragged_bf16(M, N, K, ta, tb, pad, cfg):
+    d = workloads.random_operands(M, N, K, ta, tb, seed=M * 7 + N * 3 + K, pad=pad)
+    C = run_store(d, ta, tb, M, N, K, cfg=cfg, ldc=N + 5)
+    ref = oracle_gemm_from(d, ta, tb, M, N, K)
+    got = bf16_to_f64(C[:, :N])
+    assert scaled_err(got, ref) <= GEMM_BF16_TOL
+    assert torch.isnan(C[:, N:].float()).all()          # nothing written past N
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(96, 80, 1024), (257, 300, 520), (1000, 64, 999)])
+def test_integer_valued_is_exact(M, N, K, ta, tb):
+    # entries in {-4..4}, K <= 1024: every partial sum is an integer below
+    # 2^24, so fp32 accumulation is exact in any order -> bitwise equality
+    d = workloads.random_operands(M, N, K, ta, tb, seed=K, int_range=4)
+    C = run_store(d, ta, tb, M, N, K, out_dtype=torch.float32)
+    ref = oracle_gemm_from(d, ta, tb, M, N, K)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
+
+
+def test_integer_valued_bf16_output_is_exact():
+    # |C| <= 256 keeps every integer exactly representable in bf16
+    M, N, K = 200, 136, 16
+    d = workloads.random_operands(M, N, K, "N", "T", seed=77, int_range=4)
+    C = run_store(d, "N", "T", M, N, K)
+    ref = oracle_gemm_from(d, "N", "T", M, N, K)
+    assert np.abs(ref).max() <= 256
+    assert np.array_equal(bits(C), oracle.f64_to_bf16_bits(ref))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_layouts_bitwise_identical(cfg):
+    M, N, K = 384, 320, 448
+    outs = []
+    for ta, tb in LAYOUTS:
+        d = workloads.random_operands(M, N, K, ta, tb, seed=12)
+        outs.append(run_store(d, ta, tb, M, N, K, out_dtype=torch.float32, cfg=cfg))
+    for o in outs[1:]:
+        assert torch.equal(o, outs[0])
+
+
+def test_tile_configs_agree():
+    M, N, K = 300, 260, 200
+    d = workloads.random_operands(M, N, K, "N", "T", seed=13)
+    a = run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=1)
+    b = run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=2)
+    assert torch.equal(a, b)
+
+
+def test_identity_gives_op_b():
+    K = N = 136
+    eye = torch.eye(K, dtype=torch.bfloat16)
+    d = workloads.random_operands(K, N, K, "N", "T", seed=5)
+    d = dict(d, A=eye, lda=K)
+    C = run_store(d, "N", "T", K, N, K)
+    assert torch.equal(C.cpu(), d["opB"])
+
+
+def test_nt_down_projection_full_size():
+    """768x5120x13824 NT: X [384,2,13824] flattened by view, W [5120,13824]
+    read in place; sampled rows against the oracle."""
+    w = workloads.nt_mlp()
+    X = w["X"].to(dev())
+    W = w["W"].to(dev())
+    torch.cuda.synchronize()
+    free0 = torch.cuda.mem_get_info()[0]
+    Y = tgemm.matmul(X, W.t())              # a (1, 13824)-strided view: no copy
+    torch.cuda.synchronize()
+    free1 = torch.cuda.mem_get_info()[0]
+    assert Y.shape == (384, 2, 5120)
+    # the output (7.9 MB) is the only new allocation; a transposed copy of W
+    # would need 141.6 MB
+    assert free0 - free1 < 64 * 2 ** 20
+    rows = sample_rows(768, 48, seed=2)
+    Xb = workloads.bf16_bits(w["X"]).reshape(-1)
+    Wb = workloads.bf16_bits(w["W"]).reshape(-1)
+    ref = oracle.gemm("N", "T", 768, 5120, 13824, Xb, 13824, Wb, 13824, rows=rows)
+    got = bf16_to_f64(Y.view(768, 5120)[torch.as_tensor(rows, device=dev())])
+    assert scaled_err(got, ref) <= GEMM_BF16_TOL
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+def test_layout_sweep_4096(ta, tb):
+    M = N = K = 4096
+    w = workloads.layout_sweep()
+    sa, lda = workloads.store_operand(w["opA"], ta)
+    sb, ldb = workloads.store_operand(w["opB"], tb)
+    d = {"A": sa, "lda": lda, "B": sb, "ldb": ldb}
+    C = run_store(d, ta, tb, M, N, K)
+    rows = sample_rows(M, 40, seed=3, tile=256)
+    ref = oracle.gemm(ta, tb, M, N, K, bits(sa).reshape(-1), lda, bits(sb).reshape(-1), ldb,
+                      rows=rows)
+    got = bf16_to_f64(C[torch.as_tensor(rows, device=dev())])
+    assert scaled_err(got, ref) <= GEMM_BF16_TOL
+    # every layout must give the NT bits
+    if (ta, tb) != ("N", "T"):
+        sa2, lda2 = workloads.store_operand(w["opA"], "N")
+        sb2, ldb2 = workloads.store_operand(w["opB"], "T")
+        C2 = run_store({"A": sa2, "lda": lda2, "B": sb2, "ldb": ldb2}, "N", "T", M, N, K)
+        assert torch.equal(C, C2)
+
+
+@pytest.mark.parametrize("out", ["bf16", "f32"])
+def test_k1_store_is_exact_outer_product(out):
+    M, N = 333, 77
+    for ta, tb in LAYOUTS:
+        d = workloads.random_operands(M, N, 1, ta, tb, seed=21, pad=2)
+        dt = torch.bfloat16 if out == "bf16" else torch.float32
+        C = run_store(d, ta, tb, M, N, 1, out_dtype=dt)
+        ref = oracle_gemm_from(d, ta, tb, M, N, 1)      # exact products
+        if out == "bf16":
+            assert np.array_equal(bits(C), oracle.f64_to_bf16_bits(ref))
+        else:
+            assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)

@@ -1,0 +1,89 @@
+"""GPU parity of the K=1 pointwise paths (RoPE cos/sin table, fp32 outer)."""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads
+from layout_aware_gemm_amd import tgemm
+from parity_util import K1_F32_ABS_TOL, TRIG_ABS_TOL, bf16_to_f64, bits, dev
+
+pytestmark = pytest.mark.gpu
+
+
+def check_tables(cos, sin, pos, inv_freq, rows=None):
+    pos_np = pos.cpu().numpy() if rows is None else pos.cpu().numpy()[rows]
+    _, _, rc, rs = oracle.rope_tables(pos_np, inv_freq.cpu().numpy())
+    c = bits(cos) if rows is None else bits(cos[torch.as_tensor(rows, device=cos.device)])
+    s = bits(sin) if rows is None else bits(sin[torch.as_tensor(rows, device=sin.device)])
+    dc = np.abs(oracle.bf16_bits_to_f64(c) - oracle.bf16_bits_to_f64(rc)).max()
+    ds = np.abs(oracle.bf16_bits_to_f64(s) - oracle.bf16_bits_to_f64(rs)).max()
+    assert dc <= TRIG_ABS_TOL and ds <= TRIG_ABS_TOL
+    return float(np.mean(c == rc)), float(np.mean(s == rs))
+
+
+def test_rope_table_4096x64():
+    w = workloads.rope()
+    pos, inv = w["pos"].to(dev()), w["inv_freq"].to(dev())
+    cos, sin = tgemm.rope_cos_sin(pos, inv)
+    torch.cuda.synchronize()
+    assert cos.shape == (4096, 128) and sin.shape == (4096, 128)
+    fc, fs = check_tables(cos, sin, w["pos"], w["inv_freq"])
+    assert fc > 0.99 and fs > 0.99            # nearly all bits equal
+    assert torch.equal(cos[:, :64], cos[:, 64:]) and torch.equal(sin[:, :64], sin[:, 64:])
+    assert (bits(cos[0]) == 0x3F80).all() and (bits(sin[0]) == 0).all()
+
+
+def test_rope_product_is_exact_fp32():
+    """The K=1 product itself (fp32 outer, positions cast to fp32) must equal
+    the oracle bit for bit (max abs error 0 <= 1e-5)."""
+    w = workloads.rope()
+    posf = w["pos"].to(torch.float32).to(dev())
+    inv = w["inv_freq"].to(dev())
+    t = tgemm.outer_f32(posf, inv)                      # [4096, 64]
+    torch.cuda.synchronize()
+    t19, emb, _, _ = oracle.rope_tables(w["pos"].numpy(), w["inv_freq"].numpy())
+    got = t.cpu().numpy()
+    assert np.array_equal(got, t19.T)
+    assert np.abs(got.astype(np.float64) - t19.T.astype(np.float64)).max() <= K1_F32_ABS_TOL
+
+
+def test_rope_batched_256x4096():
+    w = workloads.rope_batched(256)
+    pos, inv = w["pos"].to(dev()), w["inv_freq"].to(dev())
+    cos, sin = tgemm.rope_cos_sin(pos, inv)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    rows = np.unique(np.concatenate([np.arange(0, pos.numel(), 4099),
+                                     rng.integers(0, pos.numel(), 2000)]))
+    check_tables(cos, sin, w["pos"], w["inv_freq"], rows=rows)
+    # sequence b repeats sequence 0 exactly
+    assert torch.equal(cos[:4096], cos[4096 * 255:]) and torch.equal(sin[:4096], sin[-4096:])
+
+
+@pytest.mark.parametrize("P,F,ldc_pad", [(1, 1, 0), (37, 5, 3), (1000, 64, 8), (333, 12, 0)])
+def test_rope_ragged_and_strided(P, F, ldc_pad):
+    g = torch.Generator().manual_seed(P * F)
+    pos = torch.randint(-5000, 5000, (P,), generator=g, dtype=torch.int64)
+    inv = workloads.inv_freq(2 * F) if F > 1 else torch.tensor([1.0])
+    ldc = 2 * F + ldc_pad
+    cos = torch.full((P, ldc), float("nan"), dtype=torch.bfloat16, device=dev())
+    sin = torch.full((P, ldc), float("nan"), dtype=torch.bfloat16, device=dev())
+    # positions with an element stride of 2 and frequencies stored as an [F, 1] column
+    pos2 = torch.stack([pos, pos], 1).reshape(-1).to(dev())
+    inv2 = torch.stack([inv, inv], 1).reshape(-1).to(dev())
+    tgemm.run("N", "T", P, F, 1, pos2, 2, inv2, 2, cos, ldc, tgemm.EPI_ROPE_COSSIN, out_grad=sin)
+    torch.cuda.synchronize()
+    check_tables(cos[:, :2 * F], sin[:, :2 * F], pos, inv)
+    if ldc_pad:
+        assert torch.isnan(cos[:, 2 * F:].float()).all() and torch.isnan(sin[:, 2 * F:].float()).all()
+
+
+def test_outer_f32_random_exact():
+    rng = np.random.default_rng(3)
+    a = (rng.normal(size=513) * 100).astype(np.float32)
+    b = rng.normal(size=129).astype(np.float32)
+    c = tgemm.outer_f32(torch.from_numpy(a).to(dev()), torch.from_numpy(b).to(dev()))
+    torch.cuda.synchronize()
+    assert np.array_equal(c.cpu().numpy(), oracle.k1_outer(a, b))
