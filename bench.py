@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the layout-aware GEMM hot path on one MI355X.
+
+One step = one tgemm_run call of the NT down-projection GEMM
+Y[768,5120] = X[768,13824] . W[5120,13824]^T (X viewed from [384,2,13824], W
+read in its stored [N,K] layout, no transposed copy), inputs resident in HBM.
+Three copies of (X, W) are rotated so the 256 MB last-level cache cannot
+hold the operands between steps.  The same run also times the fused
+cross-entropy GEMM (4096 x 32000 x 4096, loss only and loss + gradient), the
+4096^3 layout sweep and the K=1 RoPE table, reported as secondary figures.
+
+Prints ONE JSON line on stdout; progress goes to stderr.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published 2.5 PF)
+PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nt_gemm_768x5120x13824_hbm_traffic.md")
+KERNEL_SOURCES = ["gemm_kernel.h", "gemm_nt.hip", "dispatch.hip"]
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "layout_aware_gemm_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary,
+    or None when the NT kernel's sources changed since it was taken."""
+    try:
+        text = open(PROFILE_COUNTERS).read()
+    except OSError:
+        return None
+    m_hash = re.search(r"kernel_source_sha256_16:\s*([0-9a-f]+)", text)
+    m_val = re.search(r"hbm_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def time_stream(fn, steps, warmup, rotate):
+    """Average ms per call, HIP events on the current stream (the one tgemm
+    launches on), bracketed by synchronisation."""
+    import torch
+
+    for i in range(warmup):
+        fn(i % rotate)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for i in range(steps):
+        fn(i % rotate)
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / steps
+
+
+def cpu_baseline(budget_s=12.0):
+    """The oracle as it stands, on the host, on a bounded sample of the NT
+    workload: whole output rows of op(A).op(B) for the first rows of X."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    w = workloads.nt_mlp()
+    M, N, K = 768, 5120, 13824
+    Xb = workloads.bf16_bits(w["X"]).reshape(-1)
+    Wb = workloads.bf16_bits(w["W"]).reshape(-1)
+    rows_done, t_total, n = 0, 0.0, 0
+    rows = np.arange(0, 96)
+    while t_total < budget_s and n < 20:
+        t0 = time.perf_counter()
+        oracle.gemm("N", "T", M, N, K, Xb, K, Wb, K, rows=rows)
+        t_total += time.perf_counter() - t0
+        rows_done += len(rows)
+        n += 1
+    flops = 2.0 * rows_done * N * K
+    return {"value": round(flops / t_total / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"{n} x fp64 oracle GEMM of 96 of 768 rows (768x5120x13824 NT, decode + "
+                      f"explicit transpose + BLAS matmul), {t_total:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--only-nt", action="store_true", help="time the NT GEMM only")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(sharding is described, not built); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import workloads
+    from layout_aware_gemm_amd import tgemm
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+    tgemm.lib()  # fails loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    K_, W_ = args.steps, args.warmup
+
+    # ---- NT down-projection: the headline step --------------------------
+    M, N, K = 768, 5120, 13824
+    flops = 2.0 * M * N * K
+    w = workloads.nt_mlp()
+    copies = 3
+    Xs = [w["X"].to(dev) for _ in range(copies)]
+    Ws = [w["W"].to(dev) for _ in range(copies)]
+    del w
+    Ys = [torch.empty(384, 2, 5120, dtype=torch.bfloat16, device=dev) for _ in range(copies)]
+    Xv = [x.view(M, K) for x in Xs]
+
+    def nt_step(i):
+        tgemm.run("N", "T", M, N, K, Xv[i], K, Ws[i], K, Ys[i], N, tgemm.EPI_STORE_BF16)
+
+    log("timing NT 768x5120x13824 ...")
+    ms = time_stream(nt_step, K_, W_, copies)
+    tflops = flops / (ms * 1e-3) / 1e12
+    ms_warm = time_stream(lambda i: nt_step(0), K_, W_, 1)
+    log(f"NT: {ms * 1e3:.1f} us/step ({tflops:.1f} TFLOP/s), same inputs: "
+        f"{ms_warm * 1e3:.1f} us")
+    del Xs, Ws, Ys, Xv
+
+    secondary = {"nt_same_inputs_us": round(ms_warm * 1e3, 2)}
+    if not args.only_nt:
+        # ---- fused cross-entropy GEMM ------------------------------------
+        Mc, Nc, Kc = 4096, 32000, 4096
+        cv = workloads.ce_vocab()
+        Hs = [cv["H"].to(dev) for _ in range(2)]
+        Wv = [cv["W"].to(dev) for _ in range(2)]
+        lab = cv["labels"].to(dev)
+        del cv
+        loss = torch.empty(Mc, dtype=torch.float32, device=dev)
+
+        def ce_step(i, g=None):
+            tgemm.run("N", "T", Mc, Nc, Kc, Hs[i], Kc, Wv[i], Kc, None, Nc, tgemm.EPI_CE,
+                      labels=lab, out_loss=loss, out_grad=g)
+
+        log("timing fused CE 4096x32000x4096 ...")
+        ms_ce = time_stream(ce_step, max(5, K_ // 5), max(2, W_ // 5), 2)
+        g = torch.empty(Mc, Nc, dtype=torch.bfloat16, device=dev)
+        ms_ceg = time_stream(lambda i: ce_step(i, g), max(5, K_ // 5), max(2, W_ // 5), 2)
+        ce_fl = 2.0 * Mc * Nc * Kc
+        secondary["ce_loss_rows_per_s"] = round(Mc / (ms_ce * 1e-3), 1)
+        secondary["ce_loss_tflops"] = round(ce_fl / (ms_ce * 1e-3) / 1e12, 2)
+        secondary["ce_loss_frac_of_peak"] = round(ce_fl / (ms_ce * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        secondary["ce_loss_ms"] = round(ms_ce, 4)
+        secondary["ce_grad_rows_per_s"] = round(Mc / (ms_ceg * 1e-3), 1)
+        secondary["ce_grad_ms"] = round(ms_ceg, 4)
+        del Hs, Wv, g
+
+        # ---- layout sweep 4096^3 ------------------------------------------
+        ls = workloads.layout_sweep()
+        for ta, tb in [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]:
+            sa, lda = workloads.store_operand(ls["opA"], ta)
+            sb, ldb = workloads.store_operand(ls["opB"], tb)
+            A, B = sa.to(dev), sb.to(dev)
+            C = torch.empty(4096, 4096, dtype=torch.bfloat16, device=dev)
+            msl = time_stream(lambda i: tgemm.run(ta, tb, 4096, 4096, 4096, A, lda, B, ldb, C,
+                                                  4096, tgemm.EPI_STORE_BF16), K_, W_, 1)
+            secondary[f"sweep_{ta}{tb}_tflops"] = round(2.0 * 4096 ** 3 / (msl * 1e-3) / 1e12, 2)
+            del A, B, C
+        del ls
+
+        # ---- K=1 RoPE table --------------------------------------------------
+        for name, r in (("rope_4096", workloads.rope()), ("rope_256x4096", workloads.rope_batched(256))):
+            pos, inv = r["pos"].to(dev), r["inv_freq"].to(dev)
+            P = pos.numel()
+            cos = torch.empty(P, 128, dtype=torch.bfloat16, device=dev)
+            sin = torch.empty_like(cos)
+            msr = time_stream(lambda i: tgemm.run("N", "N", P, 64, 1, pos, 1, inv, 64, cos, 128,
+                                                  tgemm.EPI_ROPE_COSSIN, out_grad=sin), K_, W_, 1)
+            byts = 2 * P * 128 * 2 + P * 8 + 64 * 4
+            secondary[f"{name}_us"] = round(msr * 1e3, 2)
+            secondary[f"{name}_GBps"] = round(byts / (msr * 1e-3) / 1e9, 1)
+            secondary[f"{name}_frac_of_hbm"] = round(byts / (msr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+            del pos, inv, cos, sin
+
+    traffic = measured_traffic()
+    out = {
+        "metric": "TFLOP/s and % of MFMA bf16 peak, NT 768x5120x13824; CE-fused GEMM rows/s",
+        "value": round(tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K_,
+        "warmup": W_,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded randn, bf16)",
+        "config": {"workload": "nt_down_projection_768x5120x13824",
+                   "X": "bf16[384,2,13824] viewed [768,13824]", "W": "bf16[5120,13824] read as 'T'",
+                   "rotated_input_copies": copies},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic},
+        "secondary": secondary,
+    }
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle sample ...")
+        out["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -71,6 +71,11 @@ def build(verbose=True, jobs=None):
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stdout)
+    # a library with unresolved symbols (e.g. a kernel whose host launch stub
+    # was not emitted) must not replace a working one
+    import ctypes
+
+    ctypes.CDLL(os.path.abspath(tmp), mode=os.RTLD_NOW | os.RTLD_LOCAL)
     shutil.move(tmp, LIB)
     if verbose:
         print(f"built {LIB}", file=sys.stderr)

@@ -31,11 +31,15 @@ constexpr int kThreads = 256;
 constexpr int kBK = 64;          // k elements per LDS row
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Physical 16-byte chunk of logical chunk c in LDS row `row`: XOR with a
-// 3-bit hash of the row, chosen so that (a) 8 consecutive rows reading the
-// same logical chunk and (b) rows 8 apart (the transposing writer's
-// pattern) both land in 8 distinct chunk positions.
-__device__ __forceinline__ int swz(int row) { return (row ^ (row >> 3)) & 7; }
+// Physical 16-byte chunk of logical chunk c in LDS row `row` is
+// c ^ (row & 7).  Eight consecutive rows reading the same logical chunk hit
+// eight distinct chunk positions (bank groups), and so do the writers: the
+// K-contiguous loader writes the 8 chunks of one row per 8 lanes, the
+// transposing loader writes one row per lane group with the k-chunk varying
+// fastest across lanes.  The XOR depends on the row only through row & 7,
+// so a lane's fragment addresses differ by immediate offsets across the
+// 32-row blocks it reads.
+__device__ __forceinline__ int swz(int row) { return row & 7; }
 
 __device__ __forceinline__ uint32_t u4comp(const uint4& v, int d) {
   return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
@@ -92,17 +96,21 @@ struct LoaderKMajor {
 };
 
 // Operand contiguous along M/N: stored row k holds the m (or n) index.
-// Thread t owns mn-chunk (t % CPR) (8 consecutive rows of the panel) and
-// L consecutive k; it loads L 16-byte vectors and transposes them.
+// Thread t owns k-group kb = t % KBN (L consecutive k) of mn-chunk
+// mc = t / KBN (8 consecutive rows of the panel); it loads L 16-byte vectors
+// (one per k) and transposes them.  The k-group varies fastest across lanes
+// so the transposed LDS writes of a lane group cover distinct chunks of one
+// row, while each global load instruction still covers whole 128-byte lines
+// (8 lanes with consecutive mc read 128 contiguous bytes of one k row).
 template <int R>
 struct LoaderMNMajor {
-  static constexpr int L = R / 32;   // k values per thread per k-step
-  static constexpr int CPR = R / 8;  // 8-wide mn chunks per stored k row
+  static constexpr int L = R / 32;    // k values per thread per k-step
+  static constexpr int KBN = kBK / L; // k-groups per k-step
   uint4 v[L];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int r0,
                                        int Rt, int k0, int K, bool aligned, int tid) {
-    const int mc = tid % CPR, kb = tid / CPR;
+    const int kb = tid % KBN, mc = tid / KBN;
     const int gr = r0 + mc * 8;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
@@ -127,7 +135,7 @@ struct LoaderMNMajor {
   }
 
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const int mc = tid % CPR, kb = tid / CPR;
+    const int kb = tid % KBN, mc = tid / KBN;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = mc * 8 + i;
@@ -198,6 +206,93 @@ __device__ __forceinline__ float xor_sum(float v) {
 }
 
 // ----------------------------------------------------------------------
+// Direct global -> LDS panel copy (interior tiles of K-contiguous operands).
+//
+// One wave-wide 16-byte load with the LDS destination writes 64 x 16 B =
+// 1 KB of LDS = 8 panel rows of 128 B, lane l landing at row l/8, physical
+// chunk l%8 of that block.  Each lane therefore fetches the logical chunk
+// (l%8) ^ swz(row) of its row, which produces exactly the swizzled image the
+// register path writes.  No VGPRs hold the data and no LDS write
+// instructions are issued.
+// ----------------------------------------------------------------------
+template <int R>
+struct DmaPanel {
+  static constexpr int PER_WAVE = R / 32;  // 1 KB blocks issued by each of the 4 waves
+  uint32_t off[PER_WAVE];                  // per-lane byte offsets from the panel origin
+
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int row = (wave * PER_WAVE + j) * 8 + (lane >> 3);
+      const int c = (lane & 7) ^ swz(row);
+      off[j] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+    }
+  }
+
+  // origin = &X[r0][k0] (row r0 of the tile, k-step k0), wave-uniform.
+  __device__ __forceinline__ void issue(const uint16_t* origin, uint16_t* panel,
+                                        int wave_u) const {
+#pragma unroll
+    for (int j = 0; j < PER_WAVE; ++j) {
+      const int blk = wave_u * PER_WAVE + j;
+#if defined(__HIP_DEVICE_COMPILE__)
+      // (device pass only: the host pass cannot form the LDS address-space
+      // pointer and would silently drop the kernel's launch stub)
+      __builtin_amdgcn_global_load_lds(
+          reinterpret_cast<const char*>(origin) + off[j],
+          (__attribute__((address_space(3))) void*)(panel + blk * 512), 16, 0, 0);
+#else
+      (void)origin, (void)panel, (void)blk;
+#endif
+    }
+  }
+};
+
+// Wait until every global -> LDS copy this wave issued has landed.
+__device__ __forceinline__ void wait_dma() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Operand fragments of k-substep s (k = 16s .. 16s+15) for this wave.
+// a_base / b_base: element offset of the lane's first A / B row in a stage;
+// xo[s]: swizzled element offset of the lane's 16-byte chunk in substep s.
+// Successive 32-row blocks are 32 LDS rows (4 KB) apart: immediate offsets.
+template <int FM, int FN>
+__device__ __forceinline__ void read_frags(const uint16_t* st, int a_base, int b_base, int xo,
+                                           bf16x8_t* af, bf16x8_t* bfr) {
+  const uint16_t* pa = st + a_base + xo;
+  const uint16_t* pb = st + b_base + xo;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) af[i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * kBK);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * kBK);
+}
+
+template <int FM, int FN>
+__device__ __forceinline__ void mfma_block(const bf16x8_t* af, const bf16x8_t* bfr,
+                                           f32x16_t (&acc)[FM][FN]) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+}
+
+// Scheduling pattern of one k-substep region: FM*FN MFMAs, FM+FN fragment
+// reads and NDMA global->LDS copies.  One read (and up to two copies) is
+// placed after each of the first FM+FN MFMAs; the remaining MFMAs follow.
+template <int FM, int FN, int NDMA>
+__device__ __forceinline__ void sched_substep() {
+  constexpr int NRD = FM + FN, NMF = FM * FN;
+  constexpr int DPER = (NDMA + NRD - 1) / NRD;
+#pragma unroll
+  for (int i = 0; i < NRD; ++i) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+    if constexpr (NDMA > 0) __builtin_amdgcn_sched_group_barrier(0x020, DPER, 0);  // VMEM read
+  }
+  __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
+}
+
+// ----------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI>
@@ -217,9 +312,6 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const int m0 = tm * BM, n0 = tn * BN;
   const bool aligned = p.aligned != 0;
 
-  typename LoaderSel<A_KMAJOR, BM>::type la;
-  typename LoaderSel<B_KMAJOR, BN>::type lb;
-
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -228,58 +320,103 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  // LDS offsets of this lane's operand rows.
-  int arow[FM], asw[FM], brow[FN], bsw[FN];
+  // LDS addressing of this lane's operand fragments (see read_frags).
+  const int a_base = (wm * WM + lc) * kBK;
+  const int b_base = SA + (wn * WN + lc) * kBK;
+  int xo[4];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int r = wm * WM + i * 32 + lc;
-    arow[i] = r * kBK;
-    asw[i] = swz(r);
-  }
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int r = wn * WN + j * 32 + lc;
-    brow[j] = SA + r * kBK;
-    bsw[j] = swz(r);
-  }
+  for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + h) ^ (lc & 7)) << 3;
 
-  const int nk = (p.K + kBK - 1) / kBK;
-  la.load(p.A, p.lda, m0, p.M, 0, p.K, aligned, tid);
-  lb.load(p.B, p.ldb, n0, p.N, 0, p.K, aligned, tid);
-  la.store(lds, tid);
-  lb.store(lds + SA, tid);
-  __syncthreads();
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      la.load(p.A, p.lda, m0, p.M, (kt + 1) * kBK, p.K, aligned, tid);
-      lb.load(p.B, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, aligned, tid);
-    }
-    const uint16_t* st = lds + cur * STAGE;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      bf16x8_t af[FM], bfr[FN];
-      const int c = 2 * s + h;  // logical 16-byte chunk: k = 16s + 8h .. +7
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = *reinterpret_cast<const bf16x8_t*>(st + arow[i] + ((c ^ asw[i]) << 3));
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8_t*>(st + brow[j] + ((c ^ bsw[j]) << 3));
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (more) {
-      uint16_t* nx = lds + (cur ^ 1) * STAGE;
-      la.store(nx, tid);
-      lb.store(nx + SA, tid);
-    }
+  const bool interior = aligned && m0 + BM <= p.M && n0 + BN <= p.N && (p.K % kBK) == 0 &&
+                        p.lda < (1 << 23) && p.ldb < (1 << 23);
+  if (A_KMAJOR && B_KMAJOR && interior) {
+    // Fast path: global -> LDS copies, one barrier per k-step, operand
+    // fragments double-buffered in registers so the LDS reads of the next
+    // k-substep overlap the matrix-core work of the current one.  The
+    // scheduling barriers pin that interleave: each substep region issues
+    // one fragment read (and in substep 0 the next stage's copies) between
+    // consecutive MFMAs.
+    const int nk = p.K / kBK;
+    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+    DmaPanel<BM> da;
+    DmaPanel<BN> db;
+    da.init(p.lda, wave, lane);
+    db.init(p.ldb, wave, lane);
+    const uint16_t* oa = p.A + (int64_t)m0 * p.lda;
+    const uint16_t* ob = p.B + (int64_t)n0 * p.ldb;
+    da.issue(oa, lds, wave_u);
+    db.issue(ob, lds + SA, wave_u);
+    wait_dma();
     __syncthreads();
+    bf16x8_t fa[2][FM], fb[2][FN];
+    read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint16_t* cur = lds + (kt & 1) * STAGE;
+      uint16_t* nxt = lds + ((kt & 1) ^ 1) * STAGE;
+      // substep 0 (+ next stage's copies; in the last iteration the copy
+      // re-reads the first k-step into the idle stage, unused)
+      const int kn = (kt + 1 < nk) ? (kt + 1) * kBK : 0;
+      da.issue(oa + kn, nxt, wave_u);
+      db.issue(ob + kn, nxt + SA, wave_u);
+      read_frags<FM, FN>(cur, a_base, b_base, xo[1], fa[1], fb[1]);
+      mfma_block<FM, FN>(fa[0], fb[0], acc);
+      sched_substep<FM, FN, (BM + BN) / 32>();
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 1
+      read_frags<FM, FN>(cur, a_base, b_base, xo[2], fa[0], fb[0]);
+      mfma_block<FM, FN>(fa[1], fb[1], acc);
+      sched_substep<FM, FN, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 2
+      read_frags<FM, FN>(cur, a_base, b_base, xo[3], fa[1], fb[1]);
+      mfma_block<FM, FN>(fa[0], fb[0], acc);
+      sched_substep<FM, FN, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+      // substep 3: every fragment of this stage is in registers.  The next
+      // stage's copies must have landed (own wave: vmcnt; other waves: the
+      // barrier) before it is read, and after the barrier the current stage
+      // may be overwritten by the next iteration's copies.
+      wait_dma();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+      read_frags<FM, FN>(nxt, a_base, b_base, xo[0], fa[0], fb[0]);
+      mfma_block<FM, FN>(fa[1], fb[1], acc);
+      sched_substep<FM, FN, 0>();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+    // General path: any layout, ragged edges, unaligned operands.  16-byte
+    // (or masked element) loads into registers, one k-step ahead, then
+    // (transposing if needed) stores into the other LDS stage.
+    typename LoaderSel<A_KMAJOR, BM>::type la;
+    typename LoaderSel<B_KMAJOR, BN>::type lb;
+    const int nk = (p.K + kBK - 1) / kBK;
+    la.load(p.A, p.lda, m0, p.M, 0, p.K, aligned, tid);
+    lb.load(p.B, p.ldb, n0, p.N, 0, p.K, aligned, tid);
+    la.store(lds, tid);
+    lb.store(lds + SA, tid);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        la.load(p.A, p.lda, m0, p.M, (kt + 1) * kBK, p.K, aligned, tid);
+        lb.load(p.B, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, aligned, tid);
+      }
+      const uint16_t* st = lds + cur * STAGE;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t af[FM], bfr[FN];
+        read_frags<FM, FN>(st, a_base, b_base, xo[s], af, bfr);
+        mfma_block<FM, FN>(af, bfr, acc);
+      }
+      if (more) {
+        uint16_t* nx = lds + (cur ^ 1) * STAGE;
+        la.store(nx, tid);
+        lb.store(nx + SA, tid);
+      }
+      __syncthreads();
+    }
   }
 
   // Accumulator layout of v_mfma_f32_32x32x16: lane l, register r holds
