@@ -138,11 +138,22 @@ TGEMM_API const char* tgemm_status_string(int status);
 /*
  * Tuning / testing knob: force the GEMM tile configuration for subsequent
  * calls from this process.  0 = automatic (default); 1 = 256x256 tiles;
- * 2 = 128x128 tiles.  Returns the previous value, or
- * TGEMM_ERR_INVALID_ARG for an unknown value.
+ * 2 = 128x128 tiles; 3 = 256x256 tiles on the eight-wave kernel (used when
+ * A is 'N' and B is 'T', else treated as 1).  Returns the previous value,
+ * or TGEMM_ERR_INVALID_ARG for an unknown value.
  * Not thread-safe with concurrent tgemm_run calls.
  */
 TGEMM_API int tgemm_set_tile_config(int config);
+
+/*
+ * Tuning / testing knob: force the number of K chunks a 256x256-tile GEMM
+ * with a store epilogue is split into (each chunk is a separate workgroup;
+ * partial tiles are added in ascending chunk order, so results do not
+ * depend on timing).  0 = automatic (default).  Returns the previous
+ * value, or TGEMM_ERR_INVALID_ARG outside 0..64.  Not thread-safe with
+ * concurrent tgemm_run calls.
+ */
+TGEMM_API int tgemm_set_split_k(int split);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 TGEMM_API int tgemm_version(void);

@@ -10,6 +10,7 @@ namespace tgemm {
 namespace {
 
 int g_forced_tile = kTileAuto;
+int g_forced_split = 0;
 
 inline bool is_n(char t) { return t == 'N' || t == 'n'; }
 
@@ -27,12 +28,31 @@ bool verbose() {
   return v == 1;
 }
 
-// Tile choice: 256x256 tiles when they alone give at least one tile per
-// compute unit (256 CUs), else 128x128 tiles for more parallelism.
-int choose_tile(int M, int N) {
-  if (g_forced_tile != kTileAuto) return g_forced_tile;
+// Tile choice.  256x256 tiles when they alone give most of the 256 compute
+// units a tile, otherwise 128x128 tiles.  The eight-wave kernel (kTilePP)
+// and K splitting are used only when requested.
+int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
   const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
-  return t256 >= 240 ? kTile256 : kTile128;
+  int cfg;
+  if (g_forced_tile != kTileAuto) {
+    cfg = g_forced_tile;
+    if (cfg == kTilePP && !nt) cfg = kTile256;
+  } else if (t256 >= 200) {
+    cfg = kTile256;
+  } else {
+    cfg = kTile128;
+  }
+  // K splitting is available on request (it pays only when the partial-tile
+  // traffic is small next to the main loop, which the automatic choice does
+  // not yet model); every chunk holds at least one k-step.
+  int s = 1;
+  if (cfg == kTile256 && epilogue != TGEMM_EPI_CE && g_forced_split > 0) {
+    s = g_forced_split;
+    const int max_s = ceil_div(K, 64);
+    if (s > max_s) s = max_s;
+  }
+  *split = s;
+  return cfg;
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP; }
@@ -50,8 +70,15 @@ hipError_t launch_gemm(char ta, char tb, int cfg, int epi, const GemmParams& p, 
 
 using namespace tgemm;
 
+extern "C" int tgemm_set_split_k(int split) {
+  if (split < 0 || split > 64) return TGEMM_ERR_INVALID_ARG;
+  const int prev = g_forced_split;
+  g_forced_split = split;
+  return prev;
+}
+
 extern "C" int tgemm_set_tile_config(int config) {
-  if (config < kTileAuto || config > kTile128) return TGEMM_ERR_INVALID_ARG;
+  if (config < kTileAuto || config > kTilePP) return TGEMM_ERR_INVALID_ARG;
   const int prev = g_forced_tile;
   g_forced_tile = config;
   return prev;
@@ -90,7 +117,8 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
     return status_of(e);
   }
 
-  const int cfg = choose_tile(m, n);
+  int split = 1;
+  const int cfg = choose_tile(is_n(transA) && !is_n(transB), m, n, k, epilogue, &split);
   GemmParams p = {};
   p.A = static_cast<const uint16_t*>(A);
   p.B = static_cast<const uint16_t*>(B);
@@ -102,13 +130,44 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   p.K = k;
   p.tilesM = ceil_div(M, tile_rows(cfg));
   p.tilesN = ceil_div(N, tile_cols(cfg));
-  if ((int64_t)p.tilesM * p.tilesN > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
+  p.splitk = split;
+  p.kchunk = split == 1 ? k : ceil_div(ceil_div(K, split), 64) * 64;
+  if (split > 1) p.splitk = split = ceil_div(K, p.kchunk);  // no empty chunks
+  if ((int64_t)p.tilesM * p.tilesN * p.splitk > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
   p.groupM = p.tilesM < 4 ? p.tilesM : (p.tilesM <= 8 ? p.tilesM : 4);
   p.aligned = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0 &&
               lda % 8 == 0 && ldb % 8 == 0;
   if (verbose())
-    fprintf(stderr, "tgemm: gemm %c%c M=%d N=%d K=%d tile=%d grid=%dx%d groupM=%d aligned=%d epi=%d\n",
-            transA, transB, m, n, k, cfg, p.tilesM, p.tilesN, p.groupM, p.aligned, epilogue);
+    fprintf(stderr,
+            "tgemm: gemm %c%c M=%d N=%d K=%d tile=%d grid=%dx%d split=%d (chunk %d) groupM=%d "
+            "aligned=%d epi=%d\n",
+            transA, transB, m, n, k, cfg, p.tilesM, p.tilesN, p.splitk, p.kchunk, p.groupM,
+            p.aligned, epilogue);
+
+  if (epilogue != TGEMM_EPI_CE && split > 1) {
+    // Split-K workspace: fp32 partial tiles and zeroed arrival counters,
+    // stream-ordered so concurrent calls on other streams do not share it.
+    const size_t tiles = (size_t)p.tilesM * p.tilesN;
+    const size_t tile_elems = (size_t)tile_rows(cfg) * tile_cols(cfg);
+    const size_t ws_bytes = tiles * split * tile_elems * sizeof(float);
+    const size_t cnt_bytes = ((tiles * sizeof(int) + 255) / 256) * 256;
+    char* ws = nullptr;
+    if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes + cnt_bytes, s) != hipSuccess ||
+        ws == nullptr) {
+      (void)hipGetLastError();
+      return TGEMM_ERR_NO_MEMORY;
+    }
+    p.counters = reinterpret_cast<int*>(ws);
+    p.ws = reinterpret_cast<float*>(ws + cnt_bytes);
+    p.C = C;
+    hipError_t e = hipMemsetAsync(p.counters, 0, tiles * sizeof(int), s);
+    if (e == hipSuccess)
+      e = launch_gemm(transA, transB, cfg,
+                      epilogue == TGEMM_EPI_STORE_BF16 ? kEpiStoreBf16 : kEpiStoreF32, p, s);
+    const hipError_t ef = hipFreeAsync(ws, s);
+    if (e == hipSuccess) e = ef;
+    return status_of(e);
+  }
 
   if (epilogue != TGEMM_EPI_CE) {
     p.C = C;

@@ -31,15 +31,17 @@ constexpr int kThreads = 256;
 constexpr int kBK = 64;          // k elements per LDS row
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Physical 16-byte chunk of logical chunk c in LDS row `row` is
-// c ^ (row & 7).  Eight consecutive rows reading the same logical chunk hit
-// eight distinct chunk positions (bank groups), and so do the writers: the
-// K-contiguous loader writes the 8 chunks of one row per 8 lanes, the
-// transposing loader writes one row per lane group with the k-chunk varying
-// fastest across lanes.  The XOR depends on the row only through row & 7,
-// so a lane's fragment addresses differ by immediate offsets across the
-// 32-row blocks it reads.
-__device__ __forceinline__ int swz(int row) { return row & 7; }
+// Physical 16-byte chunk of logical chunk c in LDS row `row` (128 B) is
+// c ^ ((row >> 1) & 7).  The LDS serves a 16-byte-per-lane access 16 lanes
+// at a time across 64 banks (256 B); an LDS row covers half of them, so two
+// rows of equal parity compete for the same half.  With this XOR, the 16
+// consecutive rows read by 16 lanes (same logical chunk) land in 16
+// distinct 16-byte bank groups.  The DMA writer stores 1 KB contiguously
+// per instruction and the K-contiguous loader writes two whole rows per 16
+// lanes, so both are conflict-free too.  The XOR depends on the row only
+// through (row >> 1) & 7, so a lane's fragment addresses in successive
+// 32-row blocks differ by immediate offsets.
+__device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ uint32_t u4comp(const uint4& v, int d) {
   return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
@@ -58,16 +60,16 @@ __device__ __forceinline__ uint32_t f2bf(float f) {
 // ----------------------------------------------------------------------
 
 // Operand contiguous along K: stored row r (an m or n index) holds k.
-template <int R>
+template <int R, int NTH = kThreads>
 struct LoaderKMajor {
-  static constexpr int L = R / 32;  // 16-byte chunks per thread per k-step
+  static constexpr int L = R * 8 / NTH;  // 16-byte chunks per thread per k-step
   uint4 v[L];
 
   __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int r0,
                                        int Rt, int k0, int K, bool aligned, int tid) {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int q = tid + kThreads * i;
+      const int q = tid + NTH * i;
       const int row = q >> 3, kc = q & 7;
       const int gr = r0 + row, gk = k0 + kc * 8;
       if (aligned && gr < Rt && gk + 8 <= K) {
@@ -88,7 +90,7 @@ struct LoaderKMajor {
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
 #pragma unroll
     for (int i = 0; i < L; ++i) {
-      const int q = tid + kThreads * i;
+      const int q = tid + NTH * i;
       const int row = q >> 3, kc = q & 7;
       *reinterpret_cast<uint4*>(lds + row * kBK + ((kc ^ swz(row)) << 3)) = v[i];
     }
@@ -102,9 +104,9 @@ struct LoaderKMajor {
 // so the transposed LDS writes of a lane group cover distinct chunks of one
 // row, while each global load instruction still covers whole 128-byte lines
 // (8 lanes with consecutive mc read 128 contiguous bytes of one k row).
-template <int R>
+template <int R, int NTH = kThreads>
 struct LoaderMNMajor {
-  static constexpr int L = R / 32;    // k values per thread per k-step
+  static constexpr int L = R * 8 / NTH;  // k values per thread per k-step
   static constexpr int KBN = kBK / L; // k-groups per k-step
   uint4 v[L];
 
@@ -161,35 +163,47 @@ struct LoaderMNMajor {
   }
 };
 
-template <bool KMAJOR, int R>
+template <bool KMAJOR, int R, int NTH = kThreads>
 struct LoaderSel {
-  using type = LoaderKMajor<R>;
+  using type = LoaderKMajor<R, NTH>;
 };
-template <int R>
-struct LoaderSel<false, R> {
-  using type = LoaderMNMajor<R>;
+template <int R, int NTH>
+struct LoaderSel<false, R, NTH> {
+  using type = LoaderMNMajor<R, NTH>;
 };
 
 // ----------------------------------------------------------------------
 // Workgroup -> tile mapping.  Workgroups are dealt round-robin to the 8
 // XCDs (workgroup b runs on XCD b % 8), each with its own L2.  The first
-// 8*floor(T/8) workgroups are renumbered so XCD x gets a contiguous range
-// of logical tiles; logical tiles are then ordered in groups of `groupM`
-// tile rows (column-major inside a group), so the tiles one XCD runs at
-// the same time share A rows and B columns in its L2.
+// 8*floor(W/8) workgroups are renumbered so XCD x gets a contiguous range
+// of logical workgroups; consecutive logical workgroups are the `split`
+// K chunks of one tile, then the next tile.  Tiles are ordered in groups
+// of `groupM` tile rows (column-major inside a group), so the tiles one
+// XCD runs at the same time share A rows and B columns in its L2.
 // ----------------------------------------------------------------------
-__device__ __forceinline__ void map_tile(int bid, int tilesM, int tilesN, int groupM, int& tm,
-                                         int& tn) {
-  const int T = tilesM * tilesN;
-  const int per = T >> 3;
+__device__ __forceinline__ void xcd_remap(int bid, int W, int split, int& tile, int& ks) {
+  const int per = W >> 3;
   int l = bid;
   if (bid < per * 8) l = (bid & 7) * per + (bid >> 3);
+  tile = l / split;
+  ks = l - tile * split;
+}
+
+__device__ __forceinline__ void tile_coords(int t, int tilesM, int tilesN, int groupM, int& tm,
+                                            int& tn) {
   const int gsz = groupM * tilesN;
-  const int g = l / gsz, r = l - g * gsz;
+  const int g = t / gsz, r = t - g * gsz;
   const int gm0 = g * groupM;
   const int gm = min(groupM, tilesM - gm0);
   tm = gm0 + r % gm;
   tn = r / gm;
+}
+
+__device__ __forceinline__ void map_tile(int bid, int tilesM, int tilesN, int groupM, int& tm,
+                                         int& tn) {
+  int tile, ks;
+  xcd_remap(bid, tilesM * tilesN, 1, tile, ks);
+  tile_coords(tile, tilesM, tilesN, groupM, tm, tn);
 }
 
 template <int N>
@@ -218,33 +232,50 @@ __device__ __forceinline__ float xor_sum(float v) {
 template <int R>
 struct DmaPanel {
   static constexpr int PER_WAVE = R / 32;  // 1 KB blocks issued by each of the 4 waves
-  uint32_t off[PER_WAVE];                  // per-lane byte offsets from the panel origin
+  static_assert(PER_WAVE % 2 == 0, "panel rows must be a multiple of 64");
+  // Block j of this wave covers rows (wave*PER_WAVE + j)*8 .. +7; lane l
+  // fetches row +l/8 at logical chunk (l%8) ^ swz(row).  swz(row) depends
+  // on j only through j%2, so the per-lane byte offset of block j is
+  // e[j%2] + j * 8 * ld * 2: two registers per panel, the rest is uniform.
+  uint32_t e[2];
+  int64_t row8_bytes;  // 8 rows, in bytes (uniform)
 
   __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+    const int row0 = wave * PER_WAVE * 8 + (lane >> 3);
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int row = (wave * PER_WAVE + j) * 8 + (lane >> 3);
-      const int c = (lane & 7) ^ swz(row);
-      off[j] = (uint32_t)(((int64_t)row * ld + c * 8) * 2);
+    for (int q = 0; q < 2; ++q) {
+      const int c = (lane & 7) ^ swz(row0 + 8 * q);
+      e[q] = (uint32_t)(((int64_t)row0 * ld + c * 8) * 2);
     }
+    row8_bytes = ld * 16;
   }
 
-  // origin = &X[r0][k0] (row r0 of the tile, k-step k0), wave-uniform.
+  // Copy 1 KB block j of this wave's share.  origin = &X[r0][k0] (row r0
+  // of the tile, k-step k0) and panel are wave-uniform.
+  __device__ __forceinline__ void issue_one(const uint16_t* origin, uint16_t* panel, int wave_u,
+                                            int j) const {
+    const int blk = wave_u * PER_WAVE + j;
+#if defined(__HIP_DEVICE_COMPILE__)
+    // (device pass only: the host pass cannot form the LDS address-space
+    // pointer and would silently drop the kernel's launch stub)
+    // Uniform part of the address in scalar registers, per-lane part as a
+    // 32-bit offset (the scalar-base + vector-offset addressing form).
+    const uint64_t base = reinterpret_cast<uint64_t>(origin) + (uint64_t)(j * row8_bytes);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const char* src = reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+    __builtin_amdgcn_global_load_lds(src + e[j & 1],
+                                     (__attribute__((address_space(3))) void*)(panel + blk * 512),
+                                     16, 0, 0);
+#else
+    (void)origin, (void)panel, (void)blk;
+#endif
+  }
+
   __device__ __forceinline__ void issue(const uint16_t* origin, uint16_t* panel,
                                         int wave_u) const {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) {
-      const int blk = wave_u * PER_WAVE + j;
-#if defined(__HIP_DEVICE_COMPILE__)
-      // (device pass only: the host pass cannot form the LDS address-space
-      // pointer and would silently drop the kernel's launch stub)
-      __builtin_amdgcn_global_load_lds(
-          reinterpret_cast<const char*>(origin) + off[j],
-          (__attribute__((address_space(3))) void*)(panel + blk * 512), 16, 0, 0);
-#else
-      (void)origin, (void)panel, (void)blk;
-#endif
-    }
+    for (int j = 0; j < PER_WAVE; ++j) issue_one(origin, panel, wave_u, j);
   }
 };
 
@@ -276,160 +307,230 @@ __device__ __forceinline__ void mfma_block(const bf16x8_t* af, const bf16x8_t* b
       acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
 }
 
-// Scheduling pattern of one k-substep region: FM*FN MFMAs, FM+FN fragment
-// reads and NDMA global->LDS copies.  One read (and up to two copies) is
-// placed after each of the first FM+FN MFMAs; the remaining MFMAs follow.
-template <int FM, int FN, int NDMA>
-__device__ __forceinline__ void sched_substep() {
-  constexpr int NRD = FM + FN, NMF = FM * FN;
-  constexpr int DPER = (NDMA + NRD - 1) / NRD;
+// One k-substep of the fast path, written as FM*FN issue slots.  Slot q
+// issues MFMA q of the current fragments and then its side work: the
+// fragment reads of the next substep (one per slot, first FM+FN slots) and,
+// when `dma` is set, global->LDS copies of the next stage (DPS per slot).
+// Scheduling fences between slots keep this order, so the copies and LDS
+// reads are spread between matrix-core instructions instead of bunching up.
+template <int FM, int FN, int DPS, int NA, int NB>
+__device__ __forceinline__ void substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                        const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                        const uint16_t* rd_stage, int a_base, int b_base, int xo,
+                                        bool dma, int dma0, const DmaPanel<NA * 32>& da,
+                                        const DmaPanel<NB * 32>& db, const uint16_t* oa,
+                                        const uint16_t* ob, uint16_t* dst, int wave_u) {
+  constexpr int SA = NA * 32 * kBK;
+  const uint16_t* pa = rd_stage + a_base + xo;
+  const uint16_t* pb = rd_stage + b_base + xo;
 #pragma unroll
-  for (int i = 0; i < NRD; ++i) {
-    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-    if constexpr (NDMA > 0) __builtin_amdgcn_sched_group_barrier(0x020, DPER, 0);  // VMEM read
+  for (int q = 0; q < FM * FN; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    if (dma) {
+#pragma unroll
+      for (int d = 0; d < DPS; ++d) {
+        const int n = dma0 + q * DPS + d;
+        if (n < NA) da.issue_one(oa, dst, wave_u, n);
+        else if (n < NA + NB) db.issue_one(ob, dst + SA, wave_u, n - NA);
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
   }
-  __builtin_amdgcn_sched_group_barrier(0x008, NMF - NRD, 0);
 }
 
 // ----------------------------------------------------------------------
-// The kernel.
+// Ring pipeline for interior tiles of K-contiguous operands.
+//
+// LDS holds kRingStages stages of 32 k each (A panel [BM][32] then B panel
+// [BN][32] bf16, 64-byte rows of four 16-byte chunks).  Copies of stage
+// kt+kRingStages-1 are issued while stage kt is multiplied, so a copy has
+// kRingStages-1 stages of matrix-core work (about 4000 cycles for 256x256
+// tiles) to arrive; one barrier per stage.  Logical chunk c of row r sits
+// at physical chunk c ^ ((r >> 2) & 3): sixteen lanes reading one logical
+// chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups, and
+// every copy instruction writes 1 KB of LDS contiguously.
 // ----------------------------------------------------------------------
-template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI>
-__global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
-  constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile
-  constexpr int FM = WM / 32, FN = WN / 32; // 32x32 blocks per wave
-  constexpr int SA = BM * kBK, SB = BN * kBK, STAGE = SA + SB;
-  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * STAGE];
+constexpr int kRK = 32;
+#ifndef TGEMM_RING_STAGES
+#define TGEMM_RING_STAGES 5
+#endif
+constexpr int kRingStages = TGEMM_RING_STAGES;
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int h = lane >> 5, lc = lane & 31;
+__device__ __forceinline__ int rswz(int row) { return (row >> 2) & 3; }
 
-  int tm, tn;
-  map_tile(blockIdx.x, p.tilesM, p.tilesN, p.groupM, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
-  const bool aligned = p.aligned != 0;
+// s_waitcnt immediate: vmcnt(vm), lgkmcnt(lgkm), expcnt left open.
+__host__ __device__ constexpr int waitcnt_imm(int vm, int lgkm) {
+  return (vm & 15) | ((vm >> 4) << 14) | (7 << 4) | ((lgkm & 15) << 8);
+}
 
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+template <int R>
+struct RingDma {
+  static constexpr int PER_WAVE = R / 64;  // 1 KB blocks (16 rows) per wave
+  static_assert(PER_WAVE >= 1, "panel rows must be a multiple of 64");
+  // Block j of this wave covers rows (wave*PER_WAVE + j)*16 .. +15; lane l
+  // fetches row +l/4, logical chunk (l%4) ^ rswz(row).  rswz(row) is
+  // (l/16)%4 for every block, so one per-lane offset serves all blocks.
+  uint32_t e;
+  int64_t row16_bytes;
 
-  // LDS addressing of this lane's operand fragments (see read_frags).
-  const int a_base = (wm * WM + lc) * kBK;
-  const int b_base = SA + (wn * WN + lc) * kBK;
-  int xo[4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + h) ^ (lc & 7)) << 3;
-
-  const bool interior = aligned && m0 + BM <= p.M && n0 + BN <= p.N && (p.K % kBK) == 0 &&
-                        p.lda < (1 << 23) && p.ldb < (1 << 23);
-  if (A_KMAJOR && B_KMAJOR && interior) {
-    // Fast path: global -> LDS copies, one barrier per k-step, operand
-    // fragments double-buffered in registers so the LDS reads of the next
-    // k-substep overlap the matrix-core work of the current one.  The
-    // scheduling barriers pin that interleave: each substep region issues
-    // one fragment read (and in substep 0 the next stage's copies) between
-    // consecutive MFMAs.
-    const int nk = p.K / kBK;
-    const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-    DmaPanel<BM> da;
-    DmaPanel<BN> db;
-    da.init(p.lda, wave, lane);
-    db.init(p.ldb, wave, lane);
-    const uint16_t* oa = p.A + (int64_t)m0 * p.lda;
-    const uint16_t* ob = p.B + (int64_t)n0 * p.ldb;
-    da.issue(oa, lds, wave_u);
-    db.issue(ob, lds + SA, wave_u);
-    wait_dma();
-    __syncthreads();
-    bf16x8_t fa[2][FM], fb[2][FN];
-    read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
-    for (int kt = 0; kt < nk; ++kt) {
-      const uint16_t* cur = lds + (kt & 1) * STAGE;
-      uint16_t* nxt = lds + ((kt & 1) ^ 1) * STAGE;
-      // substep 0 (+ next stage's copies; in the last iteration the copy
-      // re-reads the first k-step into the idle stage, unused)
-      const int kn = (kt + 1 < nk) ? (kt + 1) * kBK : 0;
-      da.issue(oa + kn, nxt, wave_u);
-      db.issue(ob + kn, nxt + SA, wave_u);
-      read_frags<FM, FN>(cur, a_base, b_base, xo[1], fa[1], fb[1]);
-      mfma_block<FM, FN>(fa[0], fb[0], acc);
-      sched_substep<FM, FN, (BM + BN) / 32>();
-      __builtin_amdgcn_sched_barrier(0);
-      // substep 1
-      read_frags<FM, FN>(cur, a_base, b_base, xo[2], fa[0], fb[0]);
-      mfma_block<FM, FN>(fa[1], fb[1], acc);
-      sched_substep<FM, FN, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      // substep 2
-      read_frags<FM, FN>(cur, a_base, b_base, xo[3], fa[1], fb[1]);
-      mfma_block<FM, FN>(fa[0], fb[0], acc);
-      sched_substep<FM, FN, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-      // substep 3: every fragment of this stage is in registers.  The next
-      // stage's copies must have landed (own wave: vmcnt; other waves: the
-      // barrier) before it is read, and after the barrier the current stage
-      // may be overwritten by the next iteration's copies.
-      wait_dma();
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-      read_frags<FM, FN>(nxt, a_base, b_base, xo[0], fa[0], fb[0]);
-      mfma_block<FM, FN>(fa[1], fb[1], acc);
-      sched_substep<FM, FN, 0>();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else {
-    // General path: any layout, ragged edges, unaligned operands.  16-byte
-    // (or masked element) loads into registers, one k-step ahead, then
-    // (transposing if needed) stores into the other LDS stage.
-    typename LoaderSel<A_KMAJOR, BM>::type la;
-    typename LoaderSel<B_KMAJOR, BN>::type lb;
-    const int nk = (p.K + kBK - 1) / kBK;
-    la.load(p.A, p.lda, m0, p.M, 0, p.K, aligned, tid);
-    lb.load(p.B, p.ldb, n0, p.N, 0, p.K, aligned, tid);
-    la.store(lds, tid);
-    lb.store(lds + SA, tid);
-    __syncthreads();
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      const bool more = kt + 1 < nk;
-      if (more) {
-        la.load(p.A, p.lda, m0, p.M, (kt + 1) * kBK, p.K, aligned, tid);
-        lb.load(p.B, p.ldb, n0, p.N, (kt + 1) * kBK, p.K, aligned, tid);
-      }
-      const uint16_t* st = lds + cur * STAGE;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8_t af[FM], bfr[FN];
-        read_frags<FM, FN>(st, a_base, b_base, xo[s], af, bfr);
-        mfma_block<FM, FN>(af, bfr, acc);
-      }
-      if (more) {
-        uint16_t* nx = lds + (cur ^ 1) * STAGE;
-        la.store(nx, tid);
-        lb.store(nx + SA, tid);
-      }
-      __syncthreads();
-    }
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane) {
+    const int row0 = wave * PER_WAVE * 16 + (lane >> 2);
+    const int c = (lane & 3) ^ rswz(row0);
+    e = (uint32_t)(((int64_t)row0 * ld + c * 8) * 2);
+    row16_bytes = ld * 32;
   }
 
-  // Accumulator layout of v_mfma_f32_32x32x16: lane l, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of the 32x32 block.
+  __device__ __forceinline__ void issue_one(const uint16_t* origin, uint16_t* panel, int wave_u,
+                                            int j) const {
+    const int blk = wave_u * PER_WAVE + j;
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t base = reinterpret_cast<uint64_t>(origin) + (uint64_t)(j * row16_bytes);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    const char* src = reinterpret_cast<const char*>(((uint64_t)hi << 32) | lo);
+    __builtin_amdgcn_global_load_lds(src + e,
+                                     (__attribute__((address_space(3))) void*)(panel + blk * 512),
+                                     16, 0, 0);
+#else
+    (void)origin, (void)panel, (void)blk;
+#endif
+  }
+};
+
+// One 16-k substep of the ring loop as FM*FN issue slots: MFMA q, then the
+// side work of slot q -- the next substep's fragment reads (first FM+FN
+// slots) and, if `dma`, one global->LDS copy every other slot.
+template <int FM, int FN, int NA, int NB, int BM>
+__device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                             const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                             const uint16_t* pa, const uint16_t* pb, bool dma,
+                                             const RingDma<NA * 64>& da,
+                                             const RingDma<NB * 64>& db, const uint16_t* oa,
+                                             const uint16_t* ob, uint16_t* dst, int wave_u) {
+  constexpr int RA = BM * kRK;
+#pragma unroll
+  for (int q = 0; q < FM * FN; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    // (the MFMA is issued before the slot's reads, so the wait for its own
+    // operands never covers the reads issued after it)
+    __builtin_amdgcn_sched_barrier(0);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kRK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kRK);
+    if (dma) {
+      constexpr int STEP = (FM * FN) / (NA + NB) > 0 ? (FM * FN) / (NA + NB) : 1;
+      if (q % STEP == 0) {
+        const int n = q / STEP;
+        if (n < NA) da.issue_one(oa, dst, wave_u, n);
+        else if (n < NA + NB) db.issue_one(ob, dst + RA, wave_u, n - NA);
+      }
+      if constexpr (STEP == 1 && FM * FN < NA + NB) {
+        // more copies than slots: issue the rest with the last slot
+        if (q == FM * FN - 1) {
+#pragma unroll
+          for (int n = FM * FN; n < NA + NB; ++n) {
+            if (n < NA) da.issue_one(oa, dst, wave_u, n);
+            else db.issue_one(ob, dst + RA, wave_u, n - NA);
+          }
+        }
+      }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+template <int BM, int BN, int FM, int FN>
+__device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n0,
+                                              uint16_t* lds, int wave, int lane, int wm, int wn,
+                                              f32x16_t (&acc)[FM][FN]) {
+  constexpr int RA = BM * kRK, RST = (BM + BN) * kRK, S = kRingStages;
+  constexpr int NA = BM / 64, NB = BN / 64;   // copies per wave per stage
+  constexpr int WAIT_NEXT = waitcnt_imm((NA + NB) * (S - 2), 0);
+  const int h = lane >> 5, lc = lane & 31;
+  const int nk = p.K / kRK;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  RingDma<BM> da;
+  RingDma<BN> db;
+  da.init(p.lda, wave, lane);
+  db.init(p.ldb, wave, lane);
+  const uint16_t* oa = p.A + (int64_t)m0 * p.lda;
+  const uint16_t* ob = p.B + (int64_t)n0 * p.ldb;
+  // fragment addressing inside a stage (elements)
+  const int a_off = (wm * (BM / 2) + lc) * kRK;
+  const int b_off = RA + (wn * (BN / 2) + lc) * kRK;
+  const int xo0 = ((0 + h) ^ rswz(lc)) << 3;  // substep 0: k 0..15 of the stage
+  const int xo1 = ((2 + h) ^ rswz(lc)) << 3;  // substep 1: k 16..31
+
+  // Prologue: stages 0 .. S-2.  Stages past the end of K re-read stage 0
+  // into slots that are never multiplied, which keeps the number of copies
+  // in flight (and so the vmcnt waits) uniform.
+#pragma unroll
+  for (int g = 0; g < S - 1; ++g) {
+    const int kk = (g < nk ? g : 0) * kRK;
+#pragma unroll
+    for (int j = 0; j < NA; ++j) da.issue_one(oa + kk, lds + g * RST, wave_u, j);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) db.issue_one(ob + kk, lds + g * RST + RA, wave_u, j);
+  }
+  __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+  __builtin_amdgcn_s_barrier();
+  bf16x8_t fa[2][FM], fb[2][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    fa[0][i] = *reinterpret_cast<const bf16x8_t*>(lds + a_off + xo0 + i * 32 * kRK);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    fb[0][j] = *reinterpret_cast<const bf16x8_t*>(lds + b_off + xo0 + j * 32 * kRK);
+
+  int cur = 0;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int nxt = cur + 1 == S ? 0 : cur + 1;
+    const int slot = cur == 0 ? S - 1 : cur - 1;  // freed by stage kt-1
+    const int kd = kt + S - 1;
+    const int kk = (kd < nk ? kd : 0) * kRK;
+    const uint16_t* st = lds + cur * RST;
+    __builtin_amdgcn_sched_barrier(0);
+    ring_substep<FM, FN, NA, NB, BM>(acc, fa[0], fb[0], fa[1], fb[1], st + a_off + xo1,
+                                     st + b_off + xo1, true, da, db, oa + kk, ob + kk,
+                                     lds + slot * RST, wave_u);
+    // Stage kt+1 landed (own copies: vmcnt; everyone's: the barrier), and
+    // every wave finished reading stage kt (lgkmcnt), which the copies of
+    // the next iteration overwrite.
+    __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const uint16_t* sn = lds + nxt * RST;
+    ring_substep<FM, FN, NA, NB, BM>(acc, fa[1], fb[1], fa[0], fb[0], sn + a_off + xo0,
+                                     sn + b_off + xo0, false, da, db, oa, ob, lds, wave_u);
+    cur = nxt;
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the trailing re-reads
+  __builtin_amdgcn_s_barrier();
+}
+
+// ----------------------------------------------------------------------
+// Epilogues.  Accumulator layout of v_mfma_f32_32x32x16: lane l, register r
+// holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its 32x32 block.
+// A wave owns rows m0+wr0 .. +32*FM and columns n0+wc0 .. +32*FN.
+// The caller guarantees no wave still reads LDS (the CE path reuses it).
+// ----------------------------------------------------------------------
+template <int EPI, int FM, int FN, int BM, int NTH>
+__device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM][FN], int m0,
+                                         int n0, int wr0, int wc0, int pcol, uint16_t* lds,
+                                         int tid, int lane) {
+  const int h = lane >> 5, lc = lane & 31;
   if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wn * WN + j * 32 + lc;
+        const int col = n0 + wc0 + j * 32 + lc;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const int row = m0 + wr0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (row < p.M && col < p.N) {
             if constexpr (EPI == kEpiStoreBf16)
               reinterpret_cast<uint16_t*>(p.C)[(int64_t)row * p.ldc + col] =
@@ -440,29 +541,28 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
         }
       }
   } else {
-    // Cross-entropy epilogue.  Per row of this wave's WN-column block:
-    // block max, block sum of exp(y - max), the label logit if the label
-    // column falls in the block, and optionally exp(y - block max) into
-    // the gradient buffer.  The logits themselves are not stored.
+    // Cross-entropy.  Per row of this wave's (32*FN)-column block: block
+    // max, block sum of exp(y - max), the label logit if the label column
+    // falls in the block, and optionally exp(y - block max) into the
+    // gradient buffer.  The logits themselves are not stored.
     int* slab = reinterpret_cast<int*>(lds);
-    for (int t = tid; t < BM; t += kThreads) {
+    for (int t = tid; t < BM; t += NTH) {
       const int row = m0 + t;
       slab[t] = row < p.M ? p.labels[row] : -1;
     }
     __syncthreads();
-    const int pcol = tn * 2 + wn;
     const int64_t pbase = (int64_t)pcol * p.M;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lrow = wm * WM + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+        const int lrow = wr0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
         const int row = m0 + lrow;
         const int lab = slab[lrow];
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + lc;
+          const int col = n0 + wc0 + j * 32 + lc;
           if (col < p.N) mx = fmaxf(mx, acc[i][j][r]);
         }
         mx = xor_max<32>(mx);
@@ -470,7 +570,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
         bool hit = false;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wn * WN + j * 32 + lc;
+          const int col = n0 + wc0 + j * 32 + lc;
           const float y = acc[i][j][r];
           const float e = exp2f((y - mx) * kLog2e);
           const bool ok = col < p.N;
@@ -490,10 +590,200 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
 }
 
+// ----------------------------------------------------------------------
+// Two-stage pipeline (k-step 64) for interior tiles of K-contiguous
+// operands: copies of k-step kt+1 are issued during the first substep of
+// k-step kt; one barrier per k-step.  Used for 256x256 tiles, whose LDS
+// traffic per k-step (not copy latency) bounds them, so a deeper ring buys
+// nothing there.  k-steps [k0/64, k0/64 + nk).
+// ----------------------------------------------------------------------
+template <int BM, int BN, int FM, int FN>
+__device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
+                                              uint16_t* lds, int wave, int lane, int a_base,
+                                              int b_base, const int* xo,
+                                              f32x16_t (&acc)[FM][FN]) {
+  constexpr int SA = BM * kBK, STAGE = (BM + BN) * kBK;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  DmaPanel<BM> da;
+  DmaPanel<BN> db;
+  da.init(p.lda, wave, lane);
+  db.init(p.ldb, wave, lane);
+  const uint16_t* oa = p.A + (int64_t)m0 * p.lda + k0;
+  const uint16_t* ob = p.B + (int64_t)n0 * p.ldb + k0;
+  da.issue(oa, lds, wave_u);
+  db.issue(ob, lds + SA, wave_u);
+  wait_dma();
+  __syncthreads();
+  bf16x8_t fa[2][FM], fb[2][FN];
+  read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+  constexpr int NA = BM / 32, NB = BN / 32;
+  constexpr int DPS = (NA + NB + 2 * FM * FN - 1) / (2 * FM * FN);
+  for (int kt = 0; kt < nk; ++kt) {
+    const uint16_t* cur = lds + (kt & 1) * STAGE;
+    uint16_t* nxt = lds + ((kt & 1) ^ 1) * STAGE;
+    // (in the last iteration the copy re-reads the first k-step into the
+    // idle stage, where it is never used)
+    const int kn = (kt + 1 < nk) ? (kt + 1) * kBK : 0;
+    __builtin_amdgcn_sched_barrier(0);
+    substep<FM, FN, DPS, NA, NB>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[1],
+                                 true, 0, da, db, oa + kn, ob + kn, nxt, wave_u);
+    substep<FM, FN, DPS, NA, NB>(acc, fa[1], fb[1], fa[0], fb[0], cur, a_base, b_base, xo[2],
+                                 true, FM * FN * DPS, da, db, oa + kn, ob + kn, nxt, wave_u);
+    substep<FM, FN, DPS, NA, NB>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[3],
+                                 false, 0, da, db, oa, ob, nxt, wave_u);
+    // Every fragment of this stage is in registers.  The next stage's
+    // copies must have landed (own wave: vmcnt; other waves: the barrier)
+    // before it is read, and after the barrier the current stage may be
+    // overwritten by the next iteration's copies.
+    wait_dma();
+    __syncthreads();
+    substep<FM, FN, DPS, NA, NB>(acc, fa[1], fb[1], fa[0], fb[0], nxt, a_base, b_base, xo[0],
+                                 false, 0, da, db, oa, ob, nxt, wave_u);
+  }
+}
+
+// ----------------------------------------------------------------------
+// Split-K reduction.  With p.splitk > 1 the K range is cut into splitk
+// chunks of p.kchunk elements; workgroup (tile, ks) multiplies chunk ks.
+// Every workgroup writes its fp32 partial tile to the workspace, then
+// takes a ticket on the tile's counter; the one holding the last ticket
+// (all others have written, fenced and counted by then) adds the partials
+// in ascending ks order -- a fixed order, so results are deterministic --
+// and runs the epilogue.  Returns false for the workgroups that stop.
+// ----------------------------------------------------------------------
+template <int FM, int FN, int NTH>
+__device__ __forceinline__ bool splitk_reduce(const GemmParams& p, int tile, int ks,
+                                              f32x16_t (&acc)[FM][FN], int tid, int* sflag) {
+  constexpr int PER = FM * FN * 16;  // floats per thread
+  float* mine = p.ws + ((size_t)tile * p.splitk + ks) * (size_t)(PER * NTH);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * NTH + tid] = acc[i][j][r];
+  __threadfence();
+  __syncthreads();
+  if (tid == 0) *sflag = atomicAdd(p.counters + tile, 1);
+  __syncthreads();
+  if (*sflag != p.splitk - 1) return false;
+  __threadfence();
+  const float* base = p.ws + (size_t)tile * p.splitk * (size_t)(PER * NTH);
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int idx = ((i * FN + j) * 16 + r) * NTH + tid;
+        float sum = ks == 0 ? acc[i][j][r] : __builtin_nontemporal_load(base + idx);
+        for (int q = 1; q < p.splitk; ++q)
+          sum += q == ks ? acc[i][j][r]
+                         : __builtin_nontemporal_load(base + (size_t)q * (PER * NTH) + idx);
+        acc[i][j][r] = sum;
+      }
+  if (tid == 0) p.counters[tile] = 0;  // ready for the next launch
+  return true;
+}
+
+// ----------------------------------------------------------------------
+// The kernel.
+// ----------------------------------------------------------------------
+template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI>
+__global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
+  constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile
+  constexpr int FM = WM / 32, FN = WN / 32; // 32x32 blocks per wave
+  constexpr int SA = BM * kBK, SB = BN * kBK, STAGE = SA + SB;
+  constexpr int RING = (BM + BN) * kRK * kRingStages;
+  constexpr int LDS_ELEMS = (A_KMAJOR && B_KMAJOR && RING > 2 * STAGE) ? RING : 2 * STAGE;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int h = lane >> 5, lc = lane & 31;
+
+  // workgroup -> (tile, K chunk)
+  int tile, ks;
+  xcd_remap(blockIdx.x, p.tilesM * p.tilesN * p.splitk, p.splitk, tile, ks);
+  int tm, tn;
+  tile_coords(tile, p.tilesM, p.tilesN, p.groupM, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int kbeg = ks * p.kchunk;
+  const int kend = min(p.K, kbeg + p.kchunk);
+  const bool aligned = p.aligned != 0;
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // LDS addressing of this lane's operand fragments (see read_frags).
+  const int a_base = (wm * WM + lc) * kBK;
+  const int b_base = SA + (wn * WN + lc) * kBK;
+  int xo[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + h) ^ ((lc >> 1) & 7)) << 3;
+
+  const bool interior = aligned && m0 + BM <= p.M && n0 + BN <= p.N && (kbeg % kBK) == 0 &&
+                        ((kend - kbeg) % kBK) == 0 && p.lda < (1 << 23) && p.ldb < (1 << 23);
+  if (A_KMAJOR && B_KMAJOR && interior && BM == 256) {
+    dma2_mainloop<BM, BN, FM, FN>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane, a_base,
+                                  b_base, xo, acc);
+  } else if (A_KMAJOR && B_KMAJOR && interior && p.splitk == 1) {
+    ring_mainloop<BM, BN, FM, FN>(p, m0, n0, lds, wave, lane, wm, wn, acc);
+  } else {
+    // General path: any layout, ragged edges, unaligned operands.  16-byte
+    // (or masked element) loads into registers, one k-step ahead, then
+    // (transposing if needed) stores into the other LDS stage.
+    typename LoaderSel<A_KMAJOR, BM>::type la;
+    typename LoaderSel<B_KMAJOR, BN>::type lb;
+    const int nk = (kend - kbeg + kBK - 1) / kBK;
+    la.load(p.A, p.lda, m0, p.M, kbeg, kend, aligned, tid);
+    lb.load(p.B, p.ldb, n0, p.N, kbeg, kend, aligned, tid);
+    la.store(lds, tid);
+    lb.store(lds + SA, tid);
+    __syncthreads();
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        la.load(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, aligned, tid);
+        lb.load(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, aligned, tid);
+      }
+      const uint16_t* st = lds + cur * STAGE;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        bf16x8_t af[FM], bfr[FN];
+        read_frags<FM, FN>(st, a_base, b_base, xo[s], af, bfr);
+        mfma_block<FM, FN>(af, bfr, acc);
+      }
+      if (more) {
+        uint16_t* nx = lds + (cur ^ 1) * STAGE;
+        la.store(nx, tid);
+        lb.store(nx + SA, tid);
+      }
+      __syncthreads();
+    }
+  }
+
+  __syncthreads();  // every wave is done with LDS (the CE epilogue reuses it)
+  if (p.splitk > 1) {
+    if (!splitk_reduce<FM, FN, kThreads>(p, tile, ks, acc, tid, reinterpret_cast<int*>(lds)))
+      return;
+    __syncthreads();
+  }
+  epilogue<EPI, FM, FN, BM, kThreads>(p, acc, m0, n0, wm * WM, wn * WN, tn * 2 + wn, lds, tid,
+                                      lane);
+}
+
 // Host-side launch of one instantiation.
 template <int BM, int BN, bool AK, bool BK>
 hipError_t launch_gemm_tpl(int epi, const GemmParams& p, hipStream_t s) {
-  const dim3 grid(p.tilesM * p.tilesN), block(kThreads);
+  const dim3 grid(p.tilesM * p.tilesN * p.splitk), block(kThreads);
   switch (epi) {
     case kEpiStoreBf16:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiStoreBf16>), grid, block, 0, s, p);

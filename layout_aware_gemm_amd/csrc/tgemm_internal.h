@@ -10,9 +10,11 @@ namespace tgemm {
 // Epilogue variants of the matrix-core GEMM kernel.
 enum EpiKind : int { kEpiStoreBf16 = 0, kEpiStoreF32 = 1, kEpiCE = 2 };
 
-// Tile configurations of the GEMM kernel (workgroup tile BM x BN, 4 waves in
-// a 2x2 arrangement, k-step 64).
-enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2 };
+// Tile configurations of the GEMM kernels (k-step 64):
+//   kTile256 / kTile128: BM x BN = 256x256 / 128x128, 4 waves in a 2x2 grid;
+//   kTilePP: 256x256, 8 waves in two ping-pong groups (A and B K-contiguous
+//            only), each wave 128x64.
+enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2, kTilePP = 3 };
 
 struct GemmParams {
   const uint16_t* A;  // bf16 bits
@@ -20,6 +22,10 @@ struct GemmParams {
   int64_t lda, ldb, ldc;
   int M, N, K;
   int tilesM, tilesN, groupM;
+  int splitk;         // K chunks per tile (1 = no split; store epilogues only)
+  int kchunk;         // elements of K per chunk (multiple of 64)
+  float* ws;          // split-K partial tiles [tiles][splitk][BM*BN]
+  int* counters;      // split-K arrival counters [tiles], zero between launches
   int aligned;        // A, B 16-byte aligned and lda, ldb multiples of 8
   void* C;            // store epilogues
   // cross-entropy epilogue
@@ -32,8 +38,8 @@ struct GemmParams {
 
 // Width (in columns) of the per-row partial blocks the CE epilogue writes.
 inline int ce_block_cols(int cfg) { return cfg == kTile256 ? 128 : 64; }
-inline int tile_rows(int cfg) { return cfg == kTile256 ? 256 : 128; }
-inline int tile_cols(int cfg) { return cfg == kTile256 ? 256 : 128; }
+inline int tile_rows(int cfg) { return cfg == kTile128 ? 128 : 256; }
+inline int tile_cols(int cfg) { return cfg == kTile128 ? 128 : 256; }
 
 // One launcher per operand layout (defined in gemm_<layout>.hip).
 hipError_t launch_gemm_nn(int cfg, int epi, const GemmParams& p, hipStream_t s);

@@ -30,7 +30,7 @@ EPI_OUTER_F32 = 3
 EPI_ROPE_COSSIN = 4
 
 EXPORTS = ("tgemm_run", "tgemm_validate", "tgemm_status_string", "tgemm_set_tile_config",
-           "tgemm_version")
+           "tgemm_set_split_k", "tgemm_version")
 
 
 class TgemmError(RuntimeError):
@@ -63,6 +63,8 @@ def lib():
         L.tgemm_status_string.restype = ctypes.c_char_p
         L.tgemm_set_tile_config.argtypes = [ctypes.c_int]
         L.tgemm_set_tile_config.restype = ctypes.c_int
+        L.tgemm_set_split_k.argtypes = [ctypes.c_int]
+        L.tgemm_set_split_k.restype = ctypes.c_int
         L.tgemm_version.argtypes = []
         L.tgemm_version.restype = ctypes.c_int
         _lib = L
@@ -115,10 +117,20 @@ def validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue,
 
 
 def set_tile_config(cfg):
-    """0 = automatic, 1 = 256x256, 2 = 128x128; returns the previous setting."""
+    """0 = automatic, 1 = 256x256, 2 = 128x128, 3 = 256x256 eight-wave (NT only);
+    returns the previous setting."""
     r = lib().tgemm_set_tile_config(int(cfg))
     if r < 0:
         raise TgemmError(r, "tgemm_set_tile_config")
+    return r
+
+
+def set_split_k(split):
+    """0 = automatic; s > 0 forces s K chunks for 256x256-tile store GEMMs;
+    returns the previous setting."""
+    r = lib().tgemm_set_split_k(int(split))
+    if r < 0:
+        raise TgemmError(r, "tgemm_set_split_k")
     return r
 
 

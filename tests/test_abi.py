@@ -98,6 +98,13 @@ def test_set_tile_config_roundtrip():
         tgemm.set_tile_config(9)
 
 
+def test_set_split_k_roundtrip():
+    prev = tgemm.set_split_k(4)
+    assert tgemm.set_split_k(prev) == 4
+    with pytest.raises(tgemm.TgemmError):
+        tgemm.set_split_k(-1)
+
+
 def test_layout_of_strides():
     w = torch.empty(5120, 13824, dtype=torch.bfloat16)
     assert tgemm.layout_of(w.t()) == ("T", 13824)               # weight read in place

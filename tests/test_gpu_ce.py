@@ -36,7 +36,7 @@ def oracle_ce(d, ta, tb, M, N, K, labels, rows=None):
     return oracle.cross_entropy(y, lab)
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_tiny_ce_config(cfg):
     """A bf16[64,128], W bf16[256,128]; C as fp32, loss and grad."""
     w = workloads.tiny_ce()
@@ -58,10 +58,10 @@ def test_tiny_ce_config(cfg):
 LAYOUTS = [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", [(1, 1, 1), (5, 3, 7), (70, 300, 96), (257, 520, 130),
-                                   (300, 1000, 64), (129, 64, 1)])
+                                   (300, 1000, 64), (129, 64, 1), (512, 768, 256)])
 def test_ce_ragged(M, N, K, ta, tb, cfg):
     d = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K, std=1.0, pad=1)
     g = torch.Generator().manual_seed(M * N)
