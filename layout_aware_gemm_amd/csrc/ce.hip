@@ -5,8 +5,8 @@
 // is a grid reduction (atomics or semaphores), and a cooperative launch
 // when the reduced value feeds back into other epilogue outputs.  Here the
 // GEMM epilogue leaves one (block max, block sum) pair per row and per
-// column block; `ce_combine` folds those pairs per row in ascending block
-// order (a fixed order, so the result is deterministic), and the gradient,
+// column block; `ce_combine` folds those pairs per row in a fixed order (so
+// the result is deterministic), and the gradient,
 // which needs the row's final logsumexp, is finished by `ce_grad_fixup`
 // in a second pass instead of a cooperative launch.
 #include "tgemm_internal.h"
@@ -29,28 +29,45 @@ __device__ __forceinline__ uint32_t f2bf_rne(float f) {
 
 __device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
-// One thread per row.  (m, s) (+) (m', s') = (max, s e^{m-max} + s' e^{m'-max});
-// a pair with s == 0 is the identity (-inf, 0) and is skipped.
-__global__ void __launch_bounds__(256) ce_combine_kernel(
+// (m, s) (+) (m', s') = (max, s e^{m-max} + s' e^{m'-max}); a pair with
+// s == 0 is the identity (-inf, 0) and is skipped, so -inf - -inf is never
+// evaluated.
+__device__ __forceinline__ void merge(float& m, float& s, float mt, float st) {
+  if (!(st > 0.f)) return;
+  if (s > 0.f) {
+    const float mx = fmaxf(m, mt);
+    s = s * exp_f(m - mx) + st * exp_f(mt - mx);
+    m = mx;
+  } else {
+    m = mt;
+    s = st;
+  }
+}
+
+// Workgroup = 16 rows x 16 lanes per row.  Lane q of a row folds the blocks
+// t = q, q+16, q+32, ... in ascending order; the 16 lane results are then
+// folded in ascending q.  A fixed order, so the result is deterministic.
+// Loads of one block index cover 16 consecutive rows (64 contiguous bytes).
+constexpr int kCombRows = 16, kCombParts = 16;
+
+__global__ void __launch_bounds__(kCombRows * kCombParts) ce_combine_kernel(
     const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ ylab,
     const int32_t* __restrict__ labels, int M, int N, int nblk, float* __restrict__ loss,
     float* __restrict__ lse_out) {
-  const int row = blockIdx.x * blockDim.x + threadIdx.x;
-  if (row >= M) return;
+  __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
+  const int r = threadIdx.x % kCombRows, q = threadIdx.x / kCombRows;
+  const int row = blockIdx.x * kCombRows + r;
   float m = -INFINITY, s = 0.f;
-  for (int t = 0; t < nblk; ++t) {
-    const float mt = pm[(int64_t)t * M + row];
-    const float st = ps[(int64_t)t * M + row];
-    if (!(st > 0.f)) continue;
-    if (s > 0.f) {
-      const float mx = fmaxf(m, mt);
-      s = s * exp_f(m - mx) + st * exp_f(mt - mx);
-      m = mx;
-    } else {
-      m = mt;
-      s = st;
-    }
+  if (row < M) {
+#pragma unroll 4
+    for (int t = q; t < nblk; t += kCombParts)
+      merge(m, s, pm[(int64_t)t * M + row], ps[(int64_t)t * M + row]);
   }
+  sm[q][r] = m;
+  ss[q][r] = s;
+  __syncthreads();
+  if (q != 0 || row >= M) return;
+  for (int j = 1; j < kCombParts; ++j) merge(m, s, sm[j][r], ss[j][r]);
   const float lse = m + log2f(s) * kLn2F;
   const int lab = labels[row];
   loss[row] = (lab >= 0 && lab < N) ? lse - ylab[row] : __int_as_float(0x7fc00000);
@@ -100,9 +117,9 @@ __global__ void __launch_bounds__(256) ce_grad_fixup_kernel(
 hipError_t launch_ce_combine(const float* part_m, const float* part_s, const float* ylabel,
                              const int32_t* labels, int M, int N, int nblk, float* loss,
                              float* lse, hipStream_t s) {
-  const int blocks = (M + 255) / 256;
-  hipLaunchKernelGGL(ce_combine_kernel, dim3(blocks), dim3(256), 0, s, part_m, part_s, ylabel,
-                     labels, M, N, nblk, loss, lse);
+  const int blocks = (M + kCombRows - 1) / kCombRows;
+  hipLaunchKernelGGL(ce_combine_kernel, dim3(blocks), dim3(kCombRows * kCombParts), 0, s, part_m,
+                     part_s, ylabel, labels, M, N, nblk, loss, lse);
   return hipGetLastError();
 }
 

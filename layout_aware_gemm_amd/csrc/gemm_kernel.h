@@ -297,14 +297,27 @@ __device__ __forceinline__ void read_frags(const uint16_t* st, int a_base, int b
   for (int j = 0; j < FN; ++j) bfr[j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * kBK);
 }
 
-template <int FM, int FN>
+// One 32x32x16 MFMA.  SW = false: acc block (i,j) holds C[m][n] with the
+// column n in the lane (l%32) and the row m across registers.  SW = true
+// swaps the operands, so the block holds C^T: the row m in the lane and
+// 16 columns per lane across registers (used by the cross-entropy epilogue,
+// whose row reductions then stay in registers).  Each output element is the
+// same dot product either way.
+template <bool SW>
+__device__ __forceinline__ f32x16_t mma(const bf16x8_t& a, const bf16x8_t& b, const f32x16_t& c) {
+  if constexpr (SW)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(b, a, c, 0, 0, 0);
+  else
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int FM, int FN, bool SW = false>
 __device__ __forceinline__ void mfma_block(const bf16x8_t* af, const bf16x8_t* bfr,
                                            f32x16_t (&acc)[FM][FN]) {
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < FN; ++j)
-      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+    for (int j = 0; j < FN; ++j) acc[i][j] = mma<SW>(af[i], bfr[j], acc[i][j]);
 }
 
 // One k-substep of the fast path, written as FM*FN issue slots.  Slot q
@@ -313,7 +326,7 @@ __device__ __forceinline__ void mfma_block(const bf16x8_t* af, const bf16x8_t* b
 // when `dma` is set, global->LDS copies of the next stage (DPS per slot).
 // Scheduling fences between slots keep this order, so the copies and LDS
 // reads are spread between matrix-core instructions instead of bunching up.
-template <int FM, int FN, int DPS, int NA, int NB>
+template <int FM, int FN, int DPS, int NA, int NB, bool SW = false>
 __device__ __forceinline__ void substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
                                         const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
                                         const uint16_t* rd_stage, int a_base, int b_base, int xo,
@@ -326,7 +339,7 @@ __device__ __forceinline__ void substep(f32x16_t (&acc)[FM][FN], const bf16x8_t*
 #pragma unroll
   for (int q = 0; q < FM * FN; ++q) {
     const int i = q / FN, j = q % FN;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
     if (dma) {
@@ -344,20 +357,23 @@ __device__ __forceinline__ void substep(f32x16_t (&acc)[FM][FN], const bf16x8_t*
 // ----------------------------------------------------------------------
 // Ring pipeline for interior tiles of K-contiguous operands.
 //
-// LDS holds kRingStages stages of 32 k each (A panel [BM][32] then B panel
-// [BN][32] bf16, 64-byte rows of four 16-byte chunks).  Copies of stage
-// kt+kRingStages-1 are issued while stage kt is multiplied, so a copy has
-// kRingStages-1 stages of matrix-core work (about 4000 cycles for 256x256
-// tiles) to arrive; one barrier per stage.  Logical chunk c of row r sits
+// LDS holds S = ring_stages<BM,BN>() stages of 32 k each (A panel [BM][32]
+// then B panel [BN][32] bf16, 64-byte rows of four 16-byte chunks).  Copies
+// of stage kt+S-1 are issued while stage kt is multiplied, so a copy has S-1
+// stages of matrix-core work to arrive; one barrier per stage.  Logical chunk c of row r sits
 // at physical chunk c ^ ((r >> 2) & 3): sixteen lanes reading one logical
 // chunk of 16 consecutive rows hit 16 distinct 16-byte bank groups, and
 // every copy instruction writes 1 KB of LDS contiguously.
 // ----------------------------------------------------------------------
 constexpr int kRK = 32;
-#ifndef TGEMM_RING_STAGES
-#define TGEMM_RING_STAGES 5
-#endif
-constexpr int kRingStages = TGEMM_RING_STAGES;
+constexpr int kRingLdsBytes = 160 * 1024;  // the whole LDS of a compute unit
+// Ring depth for a BM x BN tile: five 32-wide stages, or fewer if they do
+// not fit.  (Measured on the 768x5120x13824 NT GEMM with 128x128 tiles:
+// 5 stages beat 7 and 10 -- the deeper rings only add LDS footprint.)
+template <int BM, int BN>
+constexpr int ring_stages() {
+  return kRingLdsBytes / ((BM + BN) * kRK * 2) > 5 ? 5 : kRingLdsBytes / ((BM + BN) * kRK * 2);
+}
 
 __device__ __forceinline__ int rswz(int row) { return (row >> 2) & 3; }
 
@@ -403,7 +419,7 @@ struct RingDma {
 // One 16-k substep of the ring loop as FM*FN issue slots: MFMA q, then the
 // side work of slot q -- the next substep's fragment reads (first FM+FN
 // slots) and, if `dma`, one global->LDS copy every other slot.
-template <int FM, int FN, int NA, int NB, int BM>
+template <int FM, int FN, int NA, int NB, int BM, bool SW = false>
 __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
                                              const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
                                              const uint16_t* pa, const uint16_t* pb, bool dma,
@@ -414,7 +430,7 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
 #pragma unroll
   for (int q = 0; q < FM * FN; ++q) {
     const int i = q / FN, j = q % FN;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
     // (the MFMA is issued before the slot's reads, so the wait for its own
     // operands never covers the reads issued after it)
     __builtin_amdgcn_sched_barrier(0);
@@ -442,11 +458,11 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
   }
 }
 
-template <int BM, int BN, int FM, int FN>
+template <int BM, int BN, int FM, int FN, bool SW = false>
 __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n0,
                                               uint16_t* lds, int wave, int lane, int wm, int wn,
                                               f32x16_t (&acc)[FM][FN]) {
-  constexpr int RA = BM * kRK, RST = (BM + BN) * kRK, S = kRingStages;
+  constexpr int RA = BM * kRK, RST = (BM + BN) * kRK, S = ring_stages<BM, BN>();
   constexpr int NA = BM / 64, NB = BN / 64;   // copies per wave per stage
   constexpr int WAIT_NEXT = waitcnt_imm((NA + NB) * (S - 2), 0);
   const int h = lane >> 5, lc = lane & 31;
@@ -493,7 +509,7 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
     const int kk = (kd < nk ? kd : 0) * kRK;
     const uint16_t* st = lds + cur * RST;
     __builtin_amdgcn_sched_barrier(0);
-    ring_substep<FM, FN, NA, NB, BM>(acc, fa[0], fb[0], fa[1], fb[1], st + a_off + xo1,
+    ring_substep<FM, FN, NA, NB, BM, SW>(acc, fa[0], fb[0], fa[1], fb[1], st + a_off + xo1,
                                      st + b_off + xo1, true, da, db, oa + kk, ob + kk,
                                      lds + slot * RST, wave_u);
     // Stage kt+1 landed (own copies: vmcnt; everyone's: the barrier), and
@@ -503,7 +519,7 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* sn = lds + nxt * RST;
-    ring_substep<FM, FN, NA, NB, BM>(acc, fa[1], fb[1], fa[0], fb[0], sn + a_off + xo0,
+    ring_substep<FM, FN, NA, NB, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], sn + a_off + xo0,
                                      sn + b_off + xo0, false, da, db, oa, ob, lds, wave_u);
     cur = nxt;
   }
@@ -517,7 +533,7 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
 // A wave owns rows m0+wr0 .. +32*FM and columns n0+wc0 .. +32*FN.
 // The caller guarantees no wave still reads LDS (the CE path reuses it).
 // ----------------------------------------------------------------------
-template <int EPI, int FM, int FN, int BM, int NTH>
+template <int EPI, int FM, int FN, int BM, int NTH, bool SW = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM][FN], int m0,
                                          int n0, int wr0, int wc0, int pcol, uint16_t* lds,
                                          int tid, int lane) {
@@ -540,6 +556,89 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
           }
         }
       }
+  } else if constexpr (SW) {
+    // Cross-entropy on transposed accumulators: block (i,j), register r of
+    // lane l holds C[row i*32 + l%32][col j*32 + 8*(r/4) + 4*(l/32) + r%4].
+    // A lane owns 16*FN columns of one row; the other half of the wave's
+    // columns of that row sit in lane l^32.  Per row: block max, block sum
+    // of exp(y - max), the label logit if its column is in the block, and
+    // optionally exp(y - block max) into the gradient buffer (4 consecutive
+    // columns per 8-byte store).  The logits themselves are not stored.
+    int* slab = reinterpret_cast<int*>(lds);
+    for (int t = tid; t < BM; t += NTH) {
+      const int row = m0 + t;
+      slab[t] = row < p.M ? p.labels[row] : -1;
+    }
+    __syncthreads();
+    const int64_t pbase = (int64_t)pcol * p.M;
+    const bool vec8 = p.grad && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.grad) & 7) == 0;
+    float rmax[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lrow = wr0 + i * 32 + lc;
+      const int row = m0 + lrow;
+      const int lab = slab[lrow];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = n0 + wc0 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (col < p.N) mx = fmaxf(mx, acc[i][j][r]);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      float sum = 0.f, ylab = 0.f;
+      bool hit = false;
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int col = n0 + wc0 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          const float y = acc[i][j][r];
+          const float e = exp2f((y - mx) * kLog2e);
+          sum += col < p.N ? e : 0.f;
+          hit = hit || (col == lab);
+          ylab = (col == lab) ? y : ylab;
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      if (hit && row < p.M) p.ylabel[row] = ylab;
+      if (h == 0 && row < p.M) {
+        p.part_m[pbase + row] = mx;
+        p.part_s[pbase + row] = sum;
+      }
+      rmax[i] = mx;
+      // one row block at a time: keeps only its 16*FN values live
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (p.grad) {
+      // exp(y - block max) into the gradient buffer, 4 consecutive columns
+      // per 8-byte store (a separate pass, so the stores do not lengthen
+      // the live ranges of the reductions above)
+#pragma unroll
+      for (int i = 0; i < FM; ++i) {
+        const int row = m0 + wr0 + i * 32 + lc;
+        if (row >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const int col0 = n0 + wc0 + j * 32 + 8 * a + 4 * h;
+            float e[4];
+#pragma unroll
+            for (int b = 0; b < 4; ++b) e[b] = exp2f((acc[i][j][4 * a + b] - rmax[i]) * kLog2e);
+            uint16_t* g = p.grad + (int64_t)row * p.ldc + col0;
+            if (vec8 && col0 + 4 <= p.N) {
+              const uint32_t lo = f2bf(e[0]) | (f2bf(e[1]) << 16);
+              const uint32_t hi = f2bf(e[2]) | (f2bf(e[3]) << 16);
+              *reinterpret_cast<uint2*>(g) = make_uint2(lo, hi);
+            } else {
+#pragma unroll
+              for (int b = 0; b < 4; ++b)
+                if (col0 + b < p.N) g[b] = (uint16_t)f2bf(e[b]);
+            }
+          }
+      }
+    }
   } else {
     // Cross-entropy.  Per row of this wave's (32*FN)-column block: block
     // max, block sum of exp(y - max), the label logit if the label column
@@ -597,7 +696,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
 // traffic per k-step (not copy latency) bounds them, so a deeper ring buys
 // nothing there.  k-steps [k0/64, k0/64 + nk).
 // ----------------------------------------------------------------------
-template <int BM, int BN, int FM, int FN>
+template <int BM, int BN, int FM, int FN, bool SW = false>
 __device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
                                               uint16_t* lds, int wave, int lane, int a_base,
                                               int b_base, const int* xo,
@@ -625,11 +724,11 @@ __device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n
     // idle stage, where it is never used)
     const int kn = (kt + 1 < nk) ? (kt + 1) * kBK : 0;
     __builtin_amdgcn_sched_barrier(0);
-    substep<FM, FN, DPS, NA, NB>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[1],
+    substep<FM, FN, DPS, NA, NB, SW>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[1],
                                  true, 0, da, db, oa + kn, ob + kn, nxt, wave_u);
-    substep<FM, FN, DPS, NA, NB>(acc, fa[1], fb[1], fa[0], fb[0], cur, a_base, b_base, xo[2],
+    substep<FM, FN, DPS, NA, NB, SW>(acc, fa[1], fb[1], fa[0], fb[0], cur, a_base, b_base, xo[2],
                                  true, FM * FN * DPS, da, db, oa + kn, ob + kn, nxt, wave_u);
-    substep<FM, FN, DPS, NA, NB>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[3],
+    substep<FM, FN, DPS, NA, NB, SW>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[3],
                                  false, 0, da, db, oa, ob, nxt, wave_u);
     // Every fragment of this stage is in registers.  The next stage's
     // copies must have landed (own wave: vmcnt; other waves: the barrier)
@@ -637,7 +736,7 @@ __device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n
     // overwritten by the next iteration's copies.
     wait_dma();
     __syncthreads();
-    substep<FM, FN, DPS, NA, NB>(acc, fa[1], fb[1], fa[0], fb[0], nxt, a_base, b_base, xo[0],
+    substep<FM, FN, DPS, NA, NB, SW>(acc, fa[1], fb[1], fa[0], fb[0], nxt, a_base, b_base, xo[0],
                                  false, 0, da, db, oa, ob, nxt, wave_u);
   }
 }
@@ -694,7 +793,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr int WM = BM / 2, WN = BN / 2;   // wave sub-tile
   constexpr int FM = WM / 32, FN = WN / 32; // 32x32 blocks per wave
   constexpr int SA = BM * kBK, SB = BN * kBK, STAGE = SA + SB;
-  constexpr int RING = (BM + BN) * kRK * kRingStages;
+  constexpr int RING = (BM + BN) * kRK * ring_stages<BM, BN>();
+  constexpr bool SW = EPI == kEpiCE;  // transposed accumulators for row reductions
   constexpr int LDS_ELEMS = (A_KMAJOR && B_KMAJOR && RING > 2 * STAGE) ? RING : 2 * STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
 
@@ -731,10 +831,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const bool interior = aligned && m0 + BM <= p.M && n0 + BN <= p.N && (kbeg % kBK) == 0 &&
                         ((kend - kbeg) % kBK) == 0 && p.lda < (1 << 23) && p.ldb < (1 << 23);
   if (A_KMAJOR && B_KMAJOR && interior && BM == 256) {
-    dma2_mainloop<BM, BN, FM, FN>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane, a_base,
+    dma2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane, a_base,
                                   b_base, xo, acc);
   } else if (A_KMAJOR && B_KMAJOR && interior && p.splitk == 1) {
-    ring_mainloop<BM, BN, FM, FN>(p, m0, n0, lds, wave, lane, wm, wn, acc);
+    ring_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, lds, wave, lane, wm, wn, acc);
   } else {
     // General path: any layout, ragged edges, unaligned operands.  16-byte
     // (or masked element) loads into registers, one k-step ahead, then
@@ -759,7 +859,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       for (int s = 0; s < 4; ++s) {
         bf16x8_t af[FM], bfr[FN];
         read_frags<FM, FN>(st, a_base, b_base, xo[s], af, bfr);
-        mfma_block<FM, FN>(af, bfr, acc);
+        mfma_block<FM, FN, SW>(af, bfr, acc);
       }
       if (more) {
         uint16_t* nx = lds + (cur ^ 1) * STAGE;
@@ -776,8 +876,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       return;
     __syncthreads();
   }
-  epilogue<EPI, FM, FN, BM, kThreads>(p, acc, m0, n0, wm * WM, wn * WN, tn * 2 + wn, lds, tid,
-                                      lane);
+  epilogue<EPI, FM, FN, BM, kThreads, SW>(p, acc, m0, n0, wm * WM, wn * WN, tn * 2 + wn, lds, tid,
+                                          lane);
 }
 
 // Host-side launch of one instantiation.
