@@ -26,7 +26,8 @@ sys.path.insert(0, ROOT)
 PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU (published 2.5 PF)
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nt_gemm_768x5120x13824_hbm_traffic.md")
-KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pp.h", "gemm_nt.hip", "tgemm_internal.h", "dispatch.hip"]
+KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pp.h", "gemm_nt.hip", "tgemm_internal.h", "dispatch.hip",
+                  "splitk.hip"]
 COPY_CAL_BYTES = 2 ** 30  # plain device copy used to calibrate the HBM byte counters
 
 

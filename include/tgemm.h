@@ -66,7 +66,10 @@
  *   block: the block max and block sum of exponentials, plus per row the
  *   label logit and the logsumexp).  It is allocated stream-ordered
  *   (hipMallocAsync / hipFreeAsync on `stream`), so calls on different
- *   streams do not share it.
+ *   streams do not share it.  A store-epilogue GEMM whose tiles alone do
+ *   not fill the GPU (few output tiles, long K; both operands K-contiguous)
+ *   splits K into chunks and allocates one fp32 M x N partial product per
+ *   chunk the same way; a second kernel adds them in chunk order.
  */
 #ifndef TGEMM_H
 #define TGEMM_H
@@ -88,7 +91,7 @@ typedef enum {
   TGEMM_ERR_INVALID_ARG = -1, /* a flag, size, leading dimension or pointer is invalid */
   TGEMM_ERR_UNSUPPORTED = -2, /* valid request this library does not implement      */
   TGEMM_ERR_HIP = -3,         /* the HIP runtime reported an error while enqueueing   */
-  TGEMM_ERR_NO_MEMORY = -4    /* the CE workspace could not be allocated              */
+  TGEMM_ERR_NO_MEMORY = -4    /* a CE or split-K workspace could not be allocated     */
 } tgemm_status;
 
 typedef enum {
@@ -146,12 +149,13 @@ TGEMM_API const char* tgemm_status_string(int status);
 TGEMM_API int tgemm_set_tile_config(int config);
 
 /*
- * Tuning / testing knob: force the number of K chunks a 256x256-tile GEMM
- * with a store epilogue is split into (each chunk is a separate workgroup;
- * partial tiles are added in ascending chunk order, so results do not
- * depend on timing).  0 = automatic (default).  Returns the previous
- * value, or TGEMM_ERR_INVALID_ARG outside 0..64.  Not thread-safe with
- * concurrent tgemm_run calls.
+ * Tuning / testing knob: force the number of K chunks a GEMM with a store
+ * epilogue is split into (each chunk is a separate workgroup writing an
+ * fp32 partial product; a second kernel adds the partials in ascending
+ * chunk order, so results do not depend on timing).  Ignored for the CE
+ * epilogue and the eight-wave kernel.  0 = automatic (default), 1 = never
+ * split.  Returns the previous value, or TGEMM_ERR_INVALID_ARG outside
+ * 0..64.  Not thread-safe with concurrent tgemm_run calls.
  */
 TGEMM_API int tgemm_set_split_k(int split);
 

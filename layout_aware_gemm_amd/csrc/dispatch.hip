@@ -28,29 +28,41 @@ bool verbose() {
   return v == 1;
 }
 
-// Tile choice.  256x256 tiles when they alone give most of the 256 compute
-// units a tile, otherwise 128x128 tiles.  The eight-wave kernel (kTilePP)
-// and K splitting are used only when requested.
+// Tile choice.
+//  - 256x256 tiles when they alone give most of the 256 compute units a
+//    tile.
+//  - Otherwise, for a store into C with both operands K-contiguous (NT)
+//    and a long K, 256x256 tiles with K cut into `split` chunks so that
+//    tiles x split fills the chip: a 256x256 tile moves half the operand
+//    bytes per flop of a 128x128 one, which pays for writing and re-reading
+//    the fp32 partials when every chunk still spans at least 2048 of K.
+//  - Otherwise 128x128 tiles.
+// The eight-wave kernel (kTilePP) and other splits are used only when
+// requested.
 int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
   const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
-  int cfg;
+  const bool store = epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32;
+  int cfg, s = 1;
   if (g_forced_tile != kTileAuto) {
     cfg = g_forced_tile;
     if (cfg == kTilePP && !nt) cfg = kTile256;
   } else if (t256 >= 200) {
     cfg = kTile256;
   } else {
-    cfg = kTile128;
+    const int64_t fill = 256 / t256, by_k = K / 2048;
+    const int64_t auto_s = fill < by_k ? fill : by_k;
+    if (nt && store && auto_s >= 2) {
+      cfg = kTile256;
+      s = (int)auto_s;
+    } else {
+      cfg = kTile128;
+    }
   }
-  // K splitting is available on request (it pays only when the partial-tile
-  // traffic is small next to the main loop, which the automatic choice does
-  // not yet model); every chunk holds at least one k-step.
-  int s = 1;
-  if (cfg == kTile256 && epilogue != TGEMM_EPI_CE && g_forced_split > 0) {
-    s = g_forced_split;
-    const int max_s = ceil_div(K, 64);
-    if (s > max_s) s = max_s;
-  }
+  if (g_forced_split > 0) s = g_forced_split;
+  if (cfg == kTilePP || !store) s = 1;
+  // every chunk holds at least one k-step
+  const int max_s = ceil_div(K, 64);
+  if (s > max_s) s = max_s;
   *split = s;
   return cfg;
 }
@@ -145,25 +157,22 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
             p.aligned, epilogue);
 
   if (epilogue != TGEMM_EPI_CE && split > 1) {
-    // Split-K workspace: fp32 partial tiles and zeroed arrival counters,
-    // stream-ordered so concurrent calls on other streams do not share it.
-    const size_t tiles = (size_t)p.tilesM * p.tilesN;
-    const size_t tile_elems = (size_t)tile_rows(cfg) * tile_cols(cfg);
-    const size_t ws_bytes = tiles * split * tile_elems * sizeof(float);
-    const size_t cnt_bytes = ((tiles * sizeof(int) + 255) / 256) * 256;
-    char* ws = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes + cnt_bytes, s) != hipSuccess ||
+    // Split-K: one fp32 partial product per chunk, stream-ordered so
+    // concurrent calls on other streams do not share it, then the sum.
+    const size_t ws_bytes = (size_t)split * (size_t)M * (size_t)N * sizeof(float);
+    float* ws = nullptr;
+    if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s) != hipSuccess ||
         ws == nullptr) {
       (void)hipGetLastError();
       return TGEMM_ERR_NO_MEMORY;
     }
-    p.counters = reinterpret_cast<int*>(ws);
-    p.ws = reinterpret_cast<float*>(ws + cnt_bytes);
+    p.ws = ws;
     p.C = C;
-    hipError_t e = hipMemsetAsync(p.counters, 0, tiles * sizeof(int), s);
+    hipError_t e = launch_gemm(transA, transB, cfg,
+                               epilogue == TGEMM_EPI_STORE_BF16 ? kEpiStoreBf16 : kEpiStoreF32, p,
+                               s);
     if (e == hipSuccess)
-      e = launch_gemm(transA, transB, cfg,
-                      epilogue == TGEMM_EPI_STORE_BF16 ? kEpiStoreBf16 : kEpiStoreF32, p, s);
+      e = launch_splitk_sum(ws, split, m, n, C, ldc, epilogue == TGEMM_EPI_STORE_F32, s);
     const hipError_t ef = hipFreeAsync(ws, s);
     if (e == hipSuccess) e = ef;
     return status_of(e);

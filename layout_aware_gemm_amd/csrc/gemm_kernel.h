@@ -458,22 +458,22 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
   }
 }
 
+// k range [k0, k0 + nk * kRK).
 template <int BM, int BN, int FM, int FN, bool SW = false>
-__device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n0,
+__device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
                                               uint16_t* lds, int wave, int lane, int wm, int wn,
                                               f32x16_t (&acc)[FM][FN]) {
   constexpr int RA = BM * kRK, RST = (BM + BN) * kRK, S = ring_stages<BM, BN>();
   constexpr int NA = BM / 64, NB = BN / 64;   // copies per wave per stage
   constexpr int WAIT_NEXT = waitcnt_imm((NA + NB) * (S - 2), 0);
   const int h = lane >> 5, lc = lane & 31;
-  const int nk = p.K / kRK;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   RingDma<BM> da;
   RingDma<BN> db;
   da.init(p.lda, wave, lane);
   db.init(p.ldb, wave, lane);
-  const uint16_t* oa = p.A + (int64_t)m0 * p.lda;
-  const uint16_t* ob = p.B + (int64_t)n0 * p.ldb;
+  const uint16_t* oa = p.A + (int64_t)m0 * p.lda + k0;
+  const uint16_t* ob = p.B + (int64_t)n0 * p.ldb + k0;
   // fragment addressing inside a stage (elements)
   const int a_off = (wm * (BM / 2) + lc) * kRK;
   const int b_off = RA + (wn * (BN / 2) + lc) * kRK;
@@ -742,50 +742,6 @@ __device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n
 }
 
 // ----------------------------------------------------------------------
-// Split-K reduction.  With p.splitk > 1 the K range is cut into splitk
-// chunks of p.kchunk elements; workgroup (tile, ks) multiplies chunk ks.
-// Every workgroup writes its fp32 partial tile to the workspace, then
-// takes a ticket on the tile's counter; the one holding the last ticket
-// (all others have written, fenced and counted by then) adds the partials
-// in ascending ks order -- a fixed order, so results are deterministic --
-// and runs the epilogue.  Returns false for the workgroups that stop.
-// ----------------------------------------------------------------------
-template <int FM, int FN, int NTH>
-__device__ __forceinline__ bool splitk_reduce(const GemmParams& p, int tile, int ks,
-                                              f32x16_t (&acc)[FM][FN], int tid, int* sflag) {
-  constexpr int PER = FM * FN * 16;  // floats per thread
-  float* mine = p.ws + ((size_t)tile * p.splitk + ks) * (size_t)(PER * NTH);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mine[((i * FN + j) * 16 + r) * NTH + tid] = acc[i][j][r];
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) *sflag = atomicAdd(p.counters + tile, 1);
-  __syncthreads();
-  if (*sflag != p.splitk - 1) return false;
-  __threadfence();
-  const float* base = p.ws + (size_t)tile * p.splitk * (size_t)(PER * NTH);
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int idx = ((i * FN + j) * 16 + r) * NTH + tid;
-        float sum = ks == 0 ? acc[i][j][r] : __builtin_nontemporal_load(base + idx);
-        for (int q = 1; q < p.splitk; ++q)
-          sum += q == ks ? acc[i][j][r]
-                         : __builtin_nontemporal_load(base + (size_t)q * (PER * NTH) + idx);
-        acc[i][j][r] = sum;
-      }
-  if (tid == 0) p.counters[tile] = 0;  // ready for the next launch
-  return true;
-}
-
-// ----------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI>
@@ -833,8 +789,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   if (A_KMAJOR && B_KMAJOR && interior && BM == 256) {
     dma2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane, a_base,
                                   b_base, xo, acc);
-  } else if (A_KMAJOR && B_KMAJOR && interior && p.splitk == 1) {
-    ring_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, lds, wave, lane, wm, wn, acc);
+  } else if (A_KMAJOR && B_KMAJOR && interior && BM == 128) {
+    ring_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kRK, lds, wave, lane, wm,
+                                      wn, acc);
   } else {
     // General path: any layout, ragged edges, unaligned operands.  16-byte
     // (or masked element) loads into registers, one k-step ahead, then
@@ -871,10 +828,17 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
 
   __syncthreads();  // every wave is done with LDS (the CE epilogue reuses it)
-  if (p.splitk > 1) {
-    if (!splitk_reduce<FM, FN, kThreads>(p, tile, ks, acc, tid, reinterpret_cast<int*>(lds)))
+  if constexpr (EPI != kEpiCE) {
+    if (p.splitk > 1) {
+      // K chunk ks of a split product: its fp32 partial goes to slice ks of
+      // the workspace; a second kernel adds the slices in chunk order.
+      GemmParams q = p;
+      q.C = p.ws + (int64_t)ks * p.M * p.N;
+      q.ldc = p.N;
+      epilogue<kEpiStoreF32, FM, FN, BM, kThreads>(q, acc, m0, n0, wm * WM, wn * WN, 0, lds, tid,
+                                                   lane);
       return;
-    __syncthreads();
+    }
   }
   epilogue<EPI, FM, FN, BM, kThreads, SW>(p, acc, m0, n0, wm * WM, wn * WN, tn * 2 + wn, lds, tid,
                                           lane);

@@ -24,8 +24,7 @@ struct GemmParams {
   int tilesM, tilesN, groupM;
   int splitk;         // K chunks per tile (1 = no split; store epilogues only)
   int kchunk;         // elements of K per chunk (multiple of 64)
-  float* ws;          // split-K partial tiles [tiles][splitk][BM*BN]
-  int* counters;      // split-K arrival counters [tiles], zero between launches
+  float* ws;          // split-K partial products: [splitk][M][N] fp32
   int aligned;        // A, B 16-byte aligned and lda, ldb multiples of 8
   void* C;            // store epilogues
   // cross-entropy epilogue
@@ -46,6 +45,11 @@ hipError_t launch_gemm_nn(int cfg, int epi, const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_nt(int cfg, int epi, const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_tn(int cfg, int epi, const GemmParams& p, hipStream_t s);
 hipError_t launch_gemm_tt(int cfg, int epi, const GemmParams& p, hipStream_t s);
+
+// Split-K: C = sum over chunks q = 0, 1, ..., split-1 (in that order) of
+// the fp32 partial products ws[q][M][N] (defined in splitk.hip).
+hipError_t launch_splitk_sum(const float* ws, int split, int M, int N, void* C, int64_t ldc,
+                             bool out_f32, hipStream_t s);
 
 // Cross-entropy combine (per row: fold block partials in ascending block
 // order, loss = lse - y[label]) and gradient fix-up (defined in ce.hip).
