@@ -418,15 +418,21 @@ struct RingDma {
 
 // One 16-k substep of the ring loop as FM*FN issue slots: MFMA q, then the
 // side work of slot q -- the next substep's fragment reads (first FM+FN
-// slots) and, if `dma`, one global->LDS copy every other slot.
-template <int FM, int FN, int NA, int NB, int BM, bool SW = false>
+// slots) and, evenly spread over the slots, half HALF of the stage's
+// global->LDS copies.  Spreading the copies over both substeps keeps their
+// issue rate below what the texture path drains, so a wave never stalls on
+// a full copy queue while its matrix core idles.
+template <int FM, int FN, int NA, int NB, int BM, int HALF, bool SW = false>
 __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
                                              const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
-                                             const uint16_t* pa, const uint16_t* pb, bool dma,
+                                             const uint16_t* pa, const uint16_t* pb,
                                              const RingDma<NA * 64>& da,
                                              const RingDma<NB * 64>& db, const uint16_t* oa,
                                              const uint16_t* ob, uint16_t* dst, int wave_u) {
   constexpr int RA = BM * kRK;
+  constexpr int H = (NA + NB) / 2;  // copies per substep
+  static_assert((NA + NB) % 2 == 0, "copies split evenly over two substeps");
+  constexpr int STEP = (FM * FN) / H > 0 ? (FM * FN) / H : 1;
 #pragma unroll
   for (int q = 0; q < FM * FN; ++q) {
     const int i = q / FN, j = q % FN;
@@ -436,21 +442,19 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
     __builtin_amdgcn_sched_barrier(0);
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kRK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kRK);
-    if (dma) {
-      constexpr int STEP = (FM * FN) / (NA + NB) > 0 ? (FM * FN) / (NA + NB) : 1;
-      if (q % STEP == 0) {
-        const int n = q / STEP;
-        if (n < NA) da.issue_one(oa, dst, wave_u, n);
-        else if (n < NA + NB) db.issue_one(ob, dst + RA, wave_u, n - NA);
-      }
-      if constexpr (STEP == 1 && FM * FN < NA + NB) {
-        // more copies than slots: issue the rest with the last slot
-        if (q == FM * FN - 1) {
+    if (q % STEP == 0 && q / STEP < H) {
+      const int n = HALF * H + q / STEP;
+      if (n < NA) da.issue_one(oa, dst, wave_u, n);
+      else db.issue_one(ob, dst + RA, wave_u, n - NA);
+    }
+    if constexpr (STEP == 1 && FM * FN < H) {
+      // more copies than slots: issue the rest with the last slot
+      if (q == FM * FN - 1) {
 #pragma unroll
-          for (int n = FM * FN; n < NA + NB; ++n) {
-            if (n < NA) da.issue_one(oa, dst, wave_u, n);
-            else db.issue_one(ob, dst + RA, wave_u, n - NA);
-          }
+        for (int c = FM * FN; c < H; ++c) {
+          const int n = HALF * H + c;
+          if (n < NA) da.issue_one(oa, dst, wave_u, n);
+          else db.issue_one(ob, dst + RA, wave_u, n - NA);
         }
       }
     }
@@ -465,7 +469,13 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
                                               f32x16_t (&acc)[FM][FN]) {
   constexpr int RA = BM * kRK, RST = (BM + BN) * kRK, S = ring_stages<BM, BN>();
   constexpr int NA = BM / 64, NB = BN / 64;   // copies per wave per stage
-  constexpr int WAIT_NEXT = waitcnt_imm((NA + NB) * (S - 2), 0);
+  static_assert(S >= 3, "the ring needs three stages");
+  // Prologue: stage 0 landed once at most S-2 later stages are in flight.
+  // In the loop, at the wait of iteration kt (after its first substep) the
+  // copies issued after stage kt+1's are stages kt+2 .. kt+S-2 and the
+  // first half of stage kt+S-1.
+  constexpr int WAIT_FIRST = waitcnt_imm((NA + NB) * (S - 2), 0);
+  constexpr int WAIT_NEXT = waitcnt_imm((NA + NB) * (S - 3) + (NA + NB) / 2, 0);
   const int h = lane >> 5, lc = lane & 31;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   RingDma<BM> da;
@@ -491,7 +501,7 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
 #pragma unroll
     for (int j = 0; j < NB; ++j) db.issue_one(ob + kk, lds + g * RST + RA, wave_u, j);
   }
-  __builtin_amdgcn_s_waitcnt(WAIT_NEXT);
+  __builtin_amdgcn_s_waitcnt(WAIT_FIRST);
   __builtin_amdgcn_s_barrier();
   bf16x8_t fa[2][FM], fb[2][FN];
 #pragma unroll
@@ -509,9 +519,9 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
     const int kk = (kd < nk ? kd : 0) * kRK;
     const uint16_t* st = lds + cur * RST;
     __builtin_amdgcn_sched_barrier(0);
-    ring_substep<FM, FN, NA, NB, BM, SW>(acc, fa[0], fb[0], fa[1], fb[1], st + a_off + xo1,
-                                     st + b_off + xo1, true, da, db, oa + kk, ob + kk,
-                                     lds + slot * RST, wave_u);
+    ring_substep<FM, FN, NA, NB, BM, 0, SW>(acc, fa[0], fb[0], fa[1], fb[1], st + a_off + xo1,
+                                            st + b_off + xo1, da, db, oa + kk, ob + kk,
+                                            lds + slot * RST, wave_u);
     // Stage kt+1 landed (own copies: vmcnt; everyone's: the barrier), and
     // every wave finished reading stage kt (lgkmcnt), which the copies of
     // the next iteration overwrite.
@@ -519,8 +529,9 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* sn = lds + nxt * RST;
-    ring_substep<FM, FN, NA, NB, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], sn + a_off + xo0,
-                                     sn + b_off + xo0, false, da, db, oa, ob, lds, wave_u);
+    ring_substep<FM, FN, NA, NB, BM, 1, SW>(acc, fa[1], fb[1], fa[0], fb[0], sn + a_off + xo0,
+                                            sn + b_off + xo0, da, db, oa + kk, ob + kk,
+                                            lds + slot * RST, wave_u);
     cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the trailing re-reads
