@@ -27,7 +27,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU (p
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nt_gemm_768x5120x13824_hbm_traffic.md")
 KERNEL_SOURCES = ["gemm_kernel.h", "gemm_pp.h", "gemm_nt.hip", "tgemm_internal.h", "dispatch.hip",
-                  "splitk.hip"]
+                  "splitk.hip", "bf16_cvt.h"]
 COPY_CAL_BYTES = 2 ** 30  # plain device copy used to calibrate the HBM byte counters
 
 

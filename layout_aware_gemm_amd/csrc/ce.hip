@@ -9,6 +9,7 @@
 // the result is deterministic), and the gradient,
 // which needs the row's final logsumexp, is finished by `ce_grad_fixup`
 // in a second pass instead of a cooperative launch.
+#include "bf16_cvt.h"
 #include "tgemm_internal.h"
 
 namespace tgemm {
@@ -20,14 +21,6 @@ constexpr float kLn2F = 0.6931471805599453f;
 
 __device__ __forceinline__ float exp_f(float x) { return exp2f(x * kLog2eF); }
 
-__device__ __forceinline__ uint32_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
-
-__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
 
 // (m, s) (+) (m', s') = (max, s e^{m-max} + s' e^{m'-max}); a pair with
 // s == 0 is the identity (-inf, 0) and is skipped, so -inf - -inf is never
@@ -97,17 +90,17 @@ __global__ void __launch_bounds__(256) ce_grad_fixup_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = c0 + 2 * q;
-      float lo = bf2f(w[q] & 0xffffu) * scale - (c == lab ? 1.f : 0.f);
-      float hi = bf2f(w[q] >> 16) * scale - (c + 1 == lab ? 1.f : 0.f);
-      w[q] = f2bf_rne(lo) | (f2bf_rne(hi) << 16);
+      float lo = from_bf16(w[q] & 0xffffu) * scale - (c == lab ? 1.f : 0.f);
+      float hi = from_bf16(w[q] >> 16) * scale - (c + 1 == lab ? 1.f : 0.f);
+      w[q] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<uint4*>(g) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
     for (int e = 0; e < 8 && c0 + e < N; ++e) {
       const int c = c0 + e;
       const float scale = exp_f(pm[(int64_t)(c / blk_cols) * M + row] - l);
-      const float v = bf2f(g[e]) * scale - (c == lab ? 1.f : 0.f);
-      g[e] = (uint16_t)f2bf_rne(v);
+      const float v = from_bf16(g[e]) * scale - (c == lab ? 1.f : 0.f);
+      g[e] = to_bf16(v);
     }
   }
 }

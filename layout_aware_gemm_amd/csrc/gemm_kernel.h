@@ -20,6 +20,7 @@
 // on the layout, the four layouts produce bitwise-identical results.
 #pragma once
 
+#include "bf16_cvt.h"
 #include "tgemm_internal.h"
 
 namespace tgemm {
@@ -45,14 +46,6 @@ __device__ __forceinline__ int swz(int row) { return (row >> 1) & 7; }
 
 __device__ __forceinline__ uint32_t u4comp(const uint4& v, int d) {
   return d == 0 ? v.x : d == 1 ? v.y : d == 2 ? v.z : v.w;
-}
-
-// fp32 -> bf16 bits, round to nearest even, NaN kept quiet.
-__device__ __forceinline__ uint32_t f2bf(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
 }
 
 // ----------------------------------------------------------------------
@@ -561,7 +554,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
           if (row < p.M && col < p.N) {
             if constexpr (EPI == kEpiStoreBf16)
               reinterpret_cast<uint16_t*>(p.C)[(int64_t)row * p.ldc + col] =
-                  (uint16_t)f2bf(acc[i][j][r]);
+                  to_bf16(acc[i][j][r]);
             else
               reinterpret_cast<float*>(p.C)[(int64_t)row * p.ldc + col] = acc[i][j][r];
           }
@@ -639,13 +632,13 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
             for (int b = 0; b < 4; ++b) e[b] = exp2f((acc[i][j][4 * a + b] - rmax[i]) * kLog2e);
             uint16_t* g = p.grad + (int64_t)row * p.ldc + col0;
             if (vec8 && col0 + 4 <= p.N) {
-              const uint32_t lo = f2bf(e[0]) | (f2bf(e[1]) << 16);
-              const uint32_t hi = f2bf(e[2]) | (f2bf(e[3]) << 16);
+              const uint32_t lo = pack_bf16x2(e[0], e[1]);
+              const uint32_t hi = pack_bf16x2(e[2], e[3]);
               *reinterpret_cast<uint2*>(g) = make_uint2(lo, hi);
             } else {
 #pragma unroll
               for (int b = 0; b < 4; ++b)
-                if (col0 + b < p.N) g[b] = (uint16_t)f2bf(e[b]);
+                if (col0 + b < p.N) g[b] = to_bf16(e[b]);
             }
           }
       }
@@ -687,7 +680,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
           sum += ok ? e : 0.f;
           hit = hit || (col == lab);
           ylab = (col == lab) ? y : ylab;
-          if (p.grad && ok && row < p.M) p.grad[(int64_t)row * p.ldc + col] = (uint16_t)f2bf(e);
+          if (p.grad && ok && row < p.M) p.grad[(int64_t)row * p.ldc + col] = to_bf16(e);
         }
         if (hit && row < p.M) p.ylabel[row] = ylab;
         sum = xor_sum<32>(sum);

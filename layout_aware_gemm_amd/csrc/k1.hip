@@ -11,20 +11,59 @@
 // directly as [positions, 64]; fp32 multiplication commutes exactly), the
 // duplication is a second store of the same value, and everything from the
 // int64 load to the bf16 stores is one kernel.
+#include "bf16_cvt.h"
 #include "tgemm_internal.h"
 
 namespace tgemm {
 
 namespace {
 
-__device__ __forceinline__ uint32_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+
+// Largest |t| the reduced-argument sin/cos below is used for; beyond it
+// (positions past 65536 at the unit frequency, or infinities) the library
+// sincosf with its large-argument reduction is called instead.
+constexpr float kFastTrigLimit = 65536.0f;
+
+// sin(t) and cos(t) for |t| <= kFastTrigLimit, about 22 VALU operations.
+// Cody and Waite's argument reduction: t = k*pi/2 + r with k = rint(t*2/pi)
+// and pi/2 split into three fp32 parts c1 + c2 + c3 (c1 = pi/2 rounded to
+// fp32, c2 = the remainder rounded to fp32, c3 = the remainder of that;
+// what is left is 1.1e-23), subtracted with fused multiply-adds so each
+// step rounds once: |r| <= pi/4 + 0.01 and the reduction error is below
+// 1.2e-7 for every |k| <= 41722.  Then the Taylor polynomials of sin (to
+// r^9) and cos (to r^10), whose first omitted terms are below 2.1e-9 and
+// 1.4e-10 on that interval, and the quadrant k mod 4 selects and signs
+// them: sin(t) = (sin r, cos r, -sin r, -cos r), cos(t) = (cos r, -sin r,
+// -cos r, sin r) for k mod 4 = 0, 1, 2, 3.
+__device__ __forceinline__ void sincos_reduced(float t, float& sn, float& cs) {
+  const float kf = rintf(t * 0x1.45f306p-1f);              // 2/pi
+  float r = fmaf(-kf, 0x1.921fb6p+0f, t);                 // c1
+  r = fmaf(-kf, -0x1.777a5cp-25f, r);                     // c2
+  r = fmaf(-kf, -0x1.ee59dap-50f, r);                     // c3
+  const float r2 = r * r;
+  float ps = fmaf(r2, 0x1.71de3ap-19f, -0x1.a01a02p-13f);  // 1/9!, -1/7!
+  ps = fmaf(r2, ps, 0x1.111112p-7f);                      // 1/5!
+  ps = fmaf(r2, ps, -0x1.555556p-3f);                     // -1/3!
+  const float sr = fmaf(r * r2, ps, r);
+  float pc = fmaf(r2, -0x1.27e4fcp-22f, 0x1.a01a02p-16f);  // -1/10!, 1/8!
+  pc = fmaf(r2, pc, -0x1.6c16c2p-10f);                    // -1/6!
+  pc = fmaf(r2, pc, 0x1.555556p-5f);                      // 1/4!
+  pc = fmaf(r2, pc, -0.5f);                               // -1/2!
+  const float cr = fmaf(r2, pc, 1.0f);
+  const int q = (int)kf;
+  const float a = (q & 1) ? cr : sr;
+  const float b = (q & 1) ? sr : cr;
+  sn = __uint_as_float(__float_as_uint(a) ^ ((uint32_t)(q & 2) << 30));
+  cs = __uint_as_float(__float_as_uint(b) ^ ((uint32_t)((q + 1) & 2) << 30));
 }
 
-__device__ __forceinline__ float bf2f(uint32_t b) { return __uint_as_float(b << 16); }
+__device__ __forceinline__ void sincos_t(float t, float& sn, float& cs) {
+  if (fabsf(t) <= kFastTrigLimit) {
+    sincos_reduced(t, sn, cs);
+  } else {
+    sincosf(t, &sn, &cs);
+  }
+}
 
 // One thread per (row, group of 8 columns).
 __global__ void __launch_bounds__(256) k1_rope_kernel(
@@ -43,14 +82,24 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
     const float4 f0 = *reinterpret_cast<const float4*>(invf + c0);
     const float4 f1 = *reinterpret_cast<const float4*>(invf + c0 + 4);
     const float fr[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
+    float t[8], sv8[8], cv8[8], m = 0.f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      t[e] = __fmul_rn(p, fr[e]);  // one fp32 multiply, never contracted
+      m = fmaxf(m, fabsf(t[e]));
+    }
+    if (m <= kFastTrigLimit) {  // (NaN arguments take this branch and stay NaN)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sincos_reduced(t[e], sv8[e], cv8[e]);
+    } else {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sincosf(t[e], &sv8[e], &cv8[e]);
+    }
     uint32_t cw[4], sw[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      float s0, c0v, s1, c1v;
-      sincosf(__fmul_rn(p, fr[2 * q]), &s0, &c0v);
-      sincosf(__fmul_rn(p, fr[2 * q + 1]), &s1, &c1v);
-      cw[q] = f2bf_rne(c0v) | (f2bf_rne(c1v) << 16);
-      sw[q] = f2bf_rne(s0) | (f2bf_rne(s1) << 16);
+      cw[q] = pack_bf16x2(cv8[2 * q], cv8[2 * q + 1]);
+      sw[q] = pack_bf16x2(sv8[2 * q], sv8[2 * q + 1]);
     }
     const uint4 cv = make_uint4(cw[0], cw[1], cw[2], cw[3]);
     const uint4 sv = make_uint4(sw[0], sw[1], sw[2], sw[3]);
@@ -62,8 +111,8 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
     for (int e = 0; e < 8 && c0 + e < N; ++e) {
       const int c = c0 + e;
       float sv, cv;
-      sincosf(__fmul_rn(p, invf[c * sinv]), &sv, &cv);
-      const uint16_t cb = (uint16_t)f2bf_rne(cv), sb = (uint16_t)f2bf_rne(sv);
+      sincos_t(__fmul_rn(p, invf[c * sinv]), sv, cv);
+      const uint16_t cb = to_bf16(cv), sb = to_bf16(sv);
       co[c] = cb;
       co[c + N] = cb;
       so[c] = sb;
@@ -97,13 +146,13 @@ __global__ void __launch_bounds__(256) k1_outer_bf16_kernel(
   const int64_t row = gid / groups;
   if (row >= M) return;
   const int c0 = (int)(gid - row * groups) * 4;
-  const float av = bf2f(a[row * sa]);
+  const float av = from_bf16(a[row * sa]);
   for (int e = 0; e < 4 && c0 + e < N; ++e) {
-    const float v = __fmul_rn(av, bf2f(b[(int64_t)(c0 + e) * sb]));
+    const float v = __fmul_rn(av, from_bf16(b[(int64_t)(c0 + e) * sb]));
     if (out_f32)
       reinterpret_cast<float*>(C)[row * ldc + c0 + e] = v;
     else
-      reinterpret_cast<uint16_t*>(C)[row * ldc + c0 + e] = (uint16_t)f2bf_rne(v);
+      reinterpret_cast<uint16_t*>(C)[row * ldc + c0 + e] = to_bf16(v);
   }
 }
 

@@ -7,18 +7,12 @@
 // own L2, so an in-kernel hand-off needs a device-scope release (an L2
 // write-back) in every workgroup and an acquire (an L2 invalidate) in the
 // last; the kernel boundary gives the same visibility once per launch.
+#include "bf16_cvt.h"
 #include "tgemm_internal.h"
 
 namespace tgemm {
 
 namespace {
-
-__device__ __forceinline__ uint32_t f2bf_rne(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
-}
 
 // One thread: 8 consecutive columns of one row (two 16-byte loads per
 // chunk when the rows are 16-byte aligned).
@@ -64,12 +58,12 @@ __global__ void __launch_bounds__(256) splitk_sum_kernel(const float* __restrict
   if (vec_out && full) {
     uint32_t w[4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) w[e] = f2bf_rne(v[2 * e]) | (f2bf_rne(v[2 * e + 1]) << 16);
+    for (int e = 0; e < 4; ++e) w[e] = pack_bf16x2(v[2 * e], v[2 * e + 1]);
     *reinterpret_cast<uint4*>(out) = make_uint4(w[0], w[1], w[2], w[3]);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-      if (c0 + e < N) out[e] = (uint16_t)f2bf_rne(v[e]);
+      if (c0 + e < N) out[e] = to_bf16(v[e]);
   }
 }
 

@@ -35,6 +35,28 @@ def test_rope_table_4096x64():
     assert (bits(cos[0]) == 0x3F80).all() and (bits(sin[0]) == 0).all()
 
 
+@pytest.mark.parametrize("F", [64, 5])
+def test_rope_positions_across_the_reduction_range(F):
+    """Positions on both sides of the range the short argument reduction
+    serves (|t| <= 65536), negative positions and positions up to 2^24:
+    rows whose arguments all lie inside take the reduced path, the others
+    the library sincosf; every row must match the oracle."""
+    rng = np.random.default_rng(7)
+    special = [0, 1, -1, 4095, 65535, 65536, 65537, -65536, -65537, 100000, 2 ** 20,
+               2 ** 24 - 1, -(2 ** 24 - 1)]
+    pos = np.concatenate([special, rng.integers(-2 ** 24 + 1, 2 ** 24, 200),
+                          rng.integers(-70000, 70000, 300)]).astype(np.int64)
+    inv = workloads.inv_freq(2 * F) if F == 64 else torch.tensor(
+        [1.0, 0.5, 3.0e-3, 1.7, 0.25], dtype=torch.float32)
+    P = pos.size
+    pos_t = torch.from_numpy(pos)
+    cos, sin = tgemm.rope_cos_sin(pos_t.to(dev()), inv.to(dev()))
+    torch.cuda.synchronize()
+    fc, fs = check_tables(cos, sin, pos_t, inv)
+    assert fc > 0.97 and fs > 0.97
+    assert cos.shape == (P, 2 * F)
+
+
 def test_rope_product_is_exact_fp32():
     """The K=1 product itself (fp32 outer, positions cast to fp32) must equal
     the oracle bit for bit (max abs error 0 <= 1e-5)."""
