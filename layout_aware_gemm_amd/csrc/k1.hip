@@ -24,16 +24,16 @@ namespace {
 // sincosf with its large-argument reduction is called instead.
 constexpr float kFastTrigLimit = 65536.0f;
 
-// sin(t) and cos(t) for |t| <= kFastTrigLimit, about 22 VALU operations.
+// sin(t) and cos(t) for |t| <= kFastTrigLimit, about 24 VALU operations.
 // Cody and Waite's argument reduction: t = k*pi/2 + r with k = rint(t*2/pi)
 // and pi/2 split into three fp32 parts c1 + c2 + c3 (c1 = pi/2 rounded to
 // fp32, c2 = the remainder rounded to fp32, c3 = the remainder of that;
 // what is left is 1.1e-23), subtracted with fused multiply-adds so each
 // step rounds once: |r| <= pi/4 + 0.01 and the reduction error is below
 // 1.2e-7 for every |k| <= 41722.  Then the Taylor polynomials of sin (to
-// r^9) and cos (to r^10), whose first omitted terms are below 2.1e-9 and
-// 1.4e-10 on that interval, and the quadrant k mod 4 selects and signs
-// them: sin(t) = (sin r, cos r, -sin r, -cos r), cos(t) = (cos r, -sin r,
+// r^7) and cos (to r^8), whose first omitted terms are below 3.4e-7 and
+// 2.8e-8 on that interval -- far below the 2^-9 relative step of the bf16
+// results -- and the quadrant k mod 4 selects and signs them: sin(t) = (sin r, cos r, -sin r, -cos r), cos(t) = (cos r, -sin r,
 // -cos r, sin r) for k mod 4 = 0, 1, 2, 3.
 __device__ __forceinline__ void sincos_reduced(float t, float& sn, float& cs) {
   const float kf = rintf(t * 0x1.45f306p-1f);              // 2/pi
@@ -41,12 +41,10 @@ __device__ __forceinline__ void sincos_reduced(float t, float& sn, float& cs) {
   r = fmaf(-kf, -0x1.777a5cp-25f, r);                     // c2
   r = fmaf(-kf, -0x1.ee59dap-50f, r);                     // c3
   const float r2 = r * r;
-  float ps = fmaf(r2, 0x1.71de3ap-19f, -0x1.a01a02p-13f);  // 1/9!, -1/7!
-  ps = fmaf(r2, ps, 0x1.111112p-7f);                      // 1/5!
+  float ps = fmaf(r2, -0x1.a01a02p-13f, 0x1.111112p-7f);  // -1/7!, 1/5!
   ps = fmaf(r2, ps, -0x1.555556p-3f);                     // -1/3!
   const float sr = fmaf(r * r2, ps, r);
-  float pc = fmaf(r2, -0x1.27e4fcp-22f, 0x1.a01a02p-16f);  // -1/10!, 1/8!
-  pc = fmaf(r2, pc, -0x1.6c16c2p-10f);                    // -1/6!
+  float pc = fmaf(r2, 0x1.a01a02p-16f, -0x1.6c16c2p-10f);  // 1/8!, -1/6!
   pc = fmaf(r2, pc, 0x1.555556p-5f);                      // 1/4!
   pc = fmaf(r2, pc, -0.5f);                               // -1/2!
   const float cr = fmaf(r2, pc, 1.0f);
@@ -65,58 +63,87 @@ __device__ __forceinline__ void sincos_t(float t, float& sn, float& cs) {
   }
 }
 
-// One thread per (row, group of 8 columns).
+// Rows per thread of the RoPE kernel.  A thread takes RPT rows that are
+// `slots` rows apart (so the lanes of one store instruction still cover
+// consecutive rows), loads all RPT positions first and then computes and
+// stores each row: the position loads overlap each other and the trig of
+// the earlier rows.
+constexpr int kRopeRows = 2;
+
+// One thread per (row slot, group of 8 columns).
+template <int RPT>
 __global__ void __launch_bounds__(256) k1_rope_kernel(
     const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf, int64_t sinv,
     int M, int N, uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out, int64_t ldc,
     int vec_ok) {
-  const int groups = (N + 7) >> 3;
-  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  const int64_t row = gid / groups;
-  if (row >= M) return;
-  const int c0 = (int)(gid - row * groups) * 8;
-  const float p = (float)pos[row * spos];  // int64 -> fp32 (exact below 2^24)
-  uint16_t* co = cos_out + row * ldc;
-  uint16_t* so = sin_out + row * ldc;
+  // (the grid has fewer than 2^32 threads, so 32-bit index arithmetic)
+  const uint32_t groups = (uint32_t)(N + 7) >> 3;
+  const uint32_t slots = ((uint32_t)M + RPT - 1) / RPT;
+  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
+  const uint32_t rs = gid / groups;
+  if (rs >= slots) return;
+  const int c0 = (int)(gid - rs * groups) * 8;
+  float pf[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) {
+    const int64_t row = (int64_t)rs + (int64_t)j * slots;
+    const int64_t pv = row < M ? pos[row * spos] : 0;
+    // int64 -> fp32, rounded to nearest even (exact below 2^24); one
+    // instruction when the position fits in 32 bits
+    pf[j] = pv == (int64_t)(int32_t)pv ? (float)(int32_t)pv : (float)pv;
+  }
   if (vec_ok && c0 + 8 <= N) {
     const float4 f0 = *reinterpret_cast<const float4*>(invf + c0);
     const float4 f1 = *reinterpret_cast<const float4*>(invf + c0 + 4);
     const float fr[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
-    float t[8], sv8[8], cv8[8], m = 0.f;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      t[e] = __fmul_rn(p, fr[e]);  // one fp32 multiply, never contracted
-      m = fmaxf(m, fabsf(t[e]));
+    for (int j = 0; j < RPT; ++j) {
+      const int64_t row = (int64_t)rs + (int64_t)j * slots;
+      if (row >= M) break;
+      float t[8], sv8[8], cv8[8], m = 0.f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        t[e] = __fmul_rn(pf[j], fr[e]);  // one fp32 multiply, never contracted
+        m = fmaxf(m, fabsf(t[e]));
+      }
+      if (m <= kFastTrigLimit) {  // (NaN arguments take this branch and stay NaN)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sincos_reduced(t[e], sv8[e], cv8[e]);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sincosf(t[e], &sv8[e], &cv8[e]);
+      }
+      uint32_t cw[4], sw[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        cw[q] = pack_bf16x2(cv8[2 * q], cv8[2 * q + 1]);
+        sw[q] = pack_bf16x2(sv8[2 * q], sv8[2 * q + 1]);
+      }
+      const uint4 cv = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+      const uint4 sv = make_uint4(sw[0], sw[1], sw[2], sw[3]);
+      uint16_t* co = cos_out + row * ldc;
+      uint16_t* so = sin_out + row * ldc;
+      *reinterpret_cast<uint4*>(co + c0) = cv;
+      *reinterpret_cast<uint4*>(co + c0 + N) = cv;
+      *reinterpret_cast<uint4*>(so + c0) = sv;
+      *reinterpret_cast<uint4*>(so + c0 + N) = sv;
     }
-    if (m <= kFastTrigLimit) {  // (NaN arguments take this branch and stay NaN)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sincos_reduced(t[e], sv8[e], cv8[e]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) sincosf(t[e], &sv8[e], &cv8[e]);
-    }
-    uint32_t cw[4], sw[4];
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      cw[q] = pack_bf16x2(cv8[2 * q], cv8[2 * q + 1]);
-      sw[q] = pack_bf16x2(sv8[2 * q], sv8[2 * q + 1]);
-    }
-    const uint4 cv = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-    const uint4 sv = make_uint4(sw[0], sw[1], sw[2], sw[3]);
-    *reinterpret_cast<uint4*>(co + c0) = cv;
-    *reinterpret_cast<uint4*>(co + c0 + N) = cv;
-    *reinterpret_cast<uint4*>(so + c0) = sv;
-    *reinterpret_cast<uint4*>(so + c0 + N) = sv;
   } else {
-    for (int e = 0; e < 8 && c0 + e < N; ++e) {
-      const int c = c0 + e;
-      float sv, cv;
-      sincos_t(__fmul_rn(p, invf[c * sinv]), sv, cv);
-      const uint16_t cb = to_bf16(cv), sb = to_bf16(sv);
-      co[c] = cb;
-      co[c + N] = cb;
-      so[c] = sb;
-      so[c + N] = sb;
+    for (int j = 0; j < RPT; ++j) {
+      const int64_t row = (int64_t)rs + (int64_t)j * slots;
+      if (row >= M) break;
+      uint16_t* co = cos_out + row * ldc;
+      uint16_t* so = sin_out + row * ldc;
+      for (int e = 0; e < 8 && c0 + e < N; ++e) {
+        const int c = c0 + e;
+        float sv, cv;
+        sincos_t(__fmul_rn(pf[j], invf[c * sinv]), sv, cv);
+        const uint16_t cb = to_bf16(cv), sb = to_bf16(sv);
+        co[c] = cb;
+        co[c + N] = cb;
+        so[c] = sb;
+        so[c + N] = sb;
+      }
     }
   }
 }
@@ -167,9 +194,11 @@ hipError_t launch_k1_rope(const int64_t* pos, int64_t spos, const float* invf, i
                      (reinterpret_cast<uintptr_t>(cos_out) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(sin_out) & 15) == 0 && ldc % 8 == 0 &&
                      N % 8 == 0;
-  const int64_t threads = (int64_t)M * ((N + 7) / 8);
-  hipLaunchKernelGGL(k1_rope_kernel, dim3(grid_for(threads)), dim3(256), 0, s, pos, spos, invf,
-                     sinv, M, N, cos_out, sin_out, ldc, vec_ok);
+  const int64_t slots = ((int64_t)M + kRopeRows - 1) / kRopeRows;
+  const int64_t threads = slots * ((N + 7) / 8);
+  if (threads >= (int64_t(1) << 32)) return hipErrorInvalidValue;  // 32-bit thread index
+  hipLaunchKernelGGL(k1_rope_kernel<kRopeRows>, dim3(grid_for(threads)), dim3(256), 0, s, pos,
+                     spos, invf, sinv, M, N, cos_out, sin_out, ldc, vec_ok);
   return hipGetLastError();
 }
 
