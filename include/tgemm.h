@@ -64,12 +64,17 @@
  * Workspace
  *   TGEMM_EPI_CE needs a small scratch buffer (per row and per 128-column
  *   block: the block max and block sum of exponentials, plus per row the
- *   label logit and the logsumexp).  It is allocated stream-ordered
- *   (hipMallocAsync / hipFreeAsync on `stream`), so calls on different
- *   streams do not share it.  A store-epilogue GEMM whose tiles alone do
- *   not fill the GPU (few output tiles, long K; both operands K-contiguous)
- *   splits K into chunks and allocates one fp32 M x N partial product per
- *   chunk the same way; a second kernel adds them in chunk order.
+ *   label logit and the logsumexp).  A store-epilogue GEMM whose tiles
+ *   alone do not fill the GPU (few output tiles, long K; both operands
+ *   K-contiguous) splits K into chunks and needs one fp32 M x N partial
+ *   product per chunk; a second kernel adds them in chunk order.
+ *   The library keeps one workspace buffer per (device, stream): calls on
+ *   a stream run in order and reuse it; it grows with hipFreeAsync /
+ *   hipMallocAsync on that stream, so calls on different streams never
+ *   share memory.  While `stream` is being captured into a graph the call
+ *   allocates and frees its own buffer in stream order instead.  Cached
+ *   buffers are held until the process ends.  A stream must not be
+ *   destroyed while a tgemm call on it is still executing.
  */
 #ifndef TGEMM_H
 #define TGEMM_H

@@ -3,6 +3,9 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <mutex>
+#include <vector>
+
 #include "tgemm.h"
 #include "tgemm_internal.h"
 
@@ -68,6 +71,78 @@ int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
 }
 
 int status_of(hipError_t e) { return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP; }
+
+// Workspace (CE partials, split-K partial products), one buffer per
+// (device, stream).  Calls on one stream run in order, so each reuses the
+// buffer the previous call on that stream used; growing it frees the old
+// buffer and allocates the new one in stream order (hipFreeAsync /
+// hipMallocAsync on that stream), so work still queued keeps a valid
+// buffer.  Calls on different streams never share a buffer.  While the
+// stream is being captured into a graph, a call gets a buffer of its own
+// that is freed in stream order at its end (the graph owns it), exactly as
+// if there were no cache.  Cached buffers live until the process ends.
+struct Workspace {
+  void* ptr;
+  bool owned;  // free at the end of this call
+};
+
+struct WsEntry {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+
+std::mutex g_ws_mu;
+std::vector<WsEntry> g_ws;
+
+bool get_workspace(hipStream_t s, size_t bytes, Workspace* w) {
+  w->ptr = nullptr;
+  w->owned = false;
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (s != nullptr && hipStreamIsCapturing(s, &cs) == hipSuccess &&
+      cs != hipStreamCaptureStatusNone) {
+    if (hipMallocAsync(&w->ptr, bytes, s) != hipSuccess || w->ptr == nullptr) {
+      (void)hipGetLastError();
+      return false;
+    }
+    w->owned = true;
+    return true;
+  }
+  (void)hipGetLastError();
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  WsEntry* e = nullptr;
+  for (auto& x : g_ws)
+    if (x.dev == dev && x.stream == s) e = &x;
+  if (e != nullptr && e->bytes >= bytes) {
+    w->ptr = e->ptr;
+    return true;
+  }
+  // grow by at least a quarter, so a slowly growing size does not
+  // reallocate on every call
+  size_t want = bytes;
+  if (e != nullptr && want < e->bytes + e->bytes / 4) want = e->bytes + e->bytes / 4;
+  void* p = nullptr;
+  if (hipMallocAsync(&p, want, s) != hipSuccess || p == nullptr) {
+    (void)hipGetLastError();
+    return false;
+  }
+  if (e != nullptr) {
+    (void)hipFreeAsync(e->ptr, s);
+    e->ptr = p;
+    e->bytes = want;
+  } else {
+    g_ws.push_back(WsEntry{dev, s, p, want});
+  }
+  w->ptr = p;
+  return true;
+}
+
+hipError_t release_workspace(const Workspace& w, hipStream_t s) {
+  return w.owned ? hipFreeAsync(w.ptr, s) : hipSuccess;
+}
 
 hipError_t launch_gemm(char ta, char tb, int cfg, int epi, const GemmParams& p, hipStream_t s) {
   const bool an = is_n(ta), bn = is_n(tb);
@@ -157,15 +232,11 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
             p.aligned, epilogue);
 
   if (epilogue != TGEMM_EPI_CE && split > 1) {
-    // Split-K: one fp32 partial product per chunk, stream-ordered so
-    // concurrent calls on other streams do not share it, then the sum.
+    // Split-K: one fp32 partial product per chunk, then the sum.
     const size_t ws_bytes = (size_t)split * (size_t)M * (size_t)N * sizeof(float);
-    float* ws = nullptr;
-    if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_bytes, s) != hipSuccess ||
-        ws == nullptr) {
-      (void)hipGetLastError();
-      return TGEMM_ERR_NO_MEMORY;
-    }
+    Workspace w;
+    if (!get_workspace(s, ws_bytes, &w)) return TGEMM_ERR_NO_MEMORY;
+    float* ws = static_cast<float*>(w.ptr);
     p.ws = ws;
     p.C = C;
     hipError_t e = launch_gemm(transA, transB, cfg,
@@ -173,7 +244,7 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
                                s);
     if (e == hipSuccess)
       e = launch_splitk_sum(ws, split, m, n, C, ldc, epilogue == TGEMM_EPI_STORE_F32, s);
-    const hipError_t ef = hipFreeAsync(ws, s);
+    const hipError_t ef = release_workspace(w, s);
     if (e == hipSuccess) e = ef;
     return status_of(e);
   }
@@ -192,12 +263,9 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   const int blk = ce_block_cols(cfg);
   const int nblk = p.tilesN * (tile_cols(cfg) / blk);
   const size_t ws_floats = 2 * (size_t)nblk * M + 2 * (size_t)M;
-  float* ws = nullptr;
-  if (hipMallocAsync(reinterpret_cast<void**>(&ws), ws_floats * sizeof(float), s) != hipSuccess ||
-      ws == nullptr) {
-    (void)hipGetLastError();
-    return TGEMM_ERR_NO_MEMORY;
-  }
+  Workspace w;
+  if (!get_workspace(s, ws_floats * sizeof(float), &w)) return TGEMM_ERR_NO_MEMORY;
+  float* ws = static_cast<float*>(w.ptr);
   p.labels = labels;
   p.part_m = ws;
   p.part_s = ws + (size_t)nblk * M;
@@ -209,7 +277,7 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
     e = launch_ce_combine(p.part_m, p.part_s, p.ylabel, labels, m, n, nblk, out_loss, lse, s);
   if (e == hipSuccess && out_grad != nullptr)
     e = launch_ce_grad_fixup(p.grad, ldc, p.part_m, lse, labels, m, n, blk, s);
-  const hipError_t ef = hipFreeAsync(ws, s);
+  const hipError_t ef = release_workspace(w, s);
   if (e == hipSuccess) e = ef;
   return status_of(e);
 }

@@ -182,3 +182,36 @@ def test_split_k(M, N, K, split, cfg):
     assert scaled_err(bf16_to_f64(c), ref) <= GEMM_BF16_TOL
     # the bf16 output is the fp32 sum rounded once (to nearest even)
     assert np.array_equal(bits(c), oracle.f64_to_bf16_bits(a.cpu().numpy().astype(np.float64)))
+
+
+def test_streams_do_not_share_workspace():
+    """Split-K calls of different sizes in flight on two streams at once
+    (each stream has its own cached workspace) give the bits of the same
+    calls made one after another."""
+    shapes = [(256, 512, 8192), (512, 256, 6144)]
+    ds = [workloads.random_operands(M, N, K, "N", "T", seed=40 + i) for i, (M, N, K) in
+          enumerate(shapes)]
+    prev = tgemm.set_split_k(4)
+    try:
+        serial = [run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=1)
+                  for d, (M, N, K) in zip(ds, shapes)]
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        outs = []
+        prev_cfg = tgemm.set_tile_config(1)
+        try:
+            ops = [(d["A"].to(dev()), d["B"].to(dev()), d) for d in ds]
+            torch.cuda.synchronize()
+            for rep in range(3):
+                for (A, B, d), (M, N, K), st in zip(ops, shapes, streams):
+                    C = torch.empty(M, N, dtype=torch.float32, device=dev())
+                    with torch.cuda.stream(st):
+                        tgemm.run("N", "T", M, N, K, A, d["lda"], B, d["ldb"], C, N,
+                                  tgemm.EPI_STORE_F32, stream=st.cuda_stream)
+                    outs.append(C)
+            torch.cuda.synchronize()
+        finally:
+            tgemm.set_tile_config(prev_cfg)
+    finally:
+        tgemm.set_split_k(prev)
+    for i, C in enumerate(outs):
+        assert torch.equal(C, serial[i % 2])
