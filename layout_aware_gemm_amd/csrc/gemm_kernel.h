@@ -409,19 +409,59 @@ struct RingDma {
   }
 };
 
+// Ring staging of one operand, rows = its M or N extent R.  Only the
+// K-contiguous form exists (A 'N', B 'T'): a stage is the panel [R rows]
+// [32 k] copied by RingDma, and a lane's MFMA fragment (row l%32 of a
+// 32-row block, k = 8h .. 8h+7 of the 16-k substep, h = l/32) is one
+// 16-byte read.  (An MN-contiguous operand staged as k-rows and read with
+// ds_read_b64_tr_b16 needs two 8-byte reads per fragment; measured on this
+// chip, each costs about three times the issue time of a 16-byte read next
+// to the MFMAs, which made that form slower than the register path that
+// transposes while writing LDS, so MN-contiguous operands use the latter.)
+template <bool KM, int R>
+struct RingOp;
+
+template <int R>
+struct RingOp<true, R> {
+  RingDma<R> dma;
+  int f0, f1;  // element offset of the lane's fragment (block 0) in substeps 0 and 1
+
+  __device__ __forceinline__ void init(int64_t ld, int wave, int lane, int half) {
+    dma.init(ld, wave, lane);
+    const int h = lane >> 5, lc = lane & 31;
+    const int base = (half * (R / 2) + lc) * kRK;
+    f0 = base + (((0 + h) ^ rswz(lc)) << 3);
+    f1 = base + (((2 + h) ^ rswz(lc)) << 3);
+  }
+  __device__ static const uint16_t* origin(const uint16_t* X, int64_t ld, int r0, int k0) {
+    return X + (int64_t)r0 * ld + k0;
+  }
+  __device__ static int64_t kstep(int64_t, int kk) { return kk; }
+  __device__ __forceinline__ void issue_one(const uint16_t* o, uint16_t* panel, int wave_u,
+                                            int j) const {
+    dma.issue_one(o, panel, wave_u, j);
+  }
+  template <int S>
+  __device__ __forceinline__ bf16x8_t frag(const uint16_t* panel, int i) const {
+    return *reinterpret_cast<const bf16x8_t*>(panel + (S == 0 ? f0 : f1) + i * 32 * kRK);
+  }
+};
+
 // One 16-k substep of the ring loop as FM*FN issue slots: MFMA q, then the
-// side work of slot q -- the next substep's fragment reads (first FM+FN
-// slots) and, evenly spread over the slots, half HALF of the stage's
-// global->LDS copies.  Spreading the copies over both substeps keeps their
-// issue rate below what the texture path drains, so a wave never stalls on
-// a full copy queue while its matrix core idles.
-template <int FM, int FN, int NA, int NB, int BM, int HALF, bool SW = false>
+// side work of slot q -- the fragment reads of substep RS of the panel
+// stage `ra_st`/`rb_st` (first FM+FN slots) and, evenly spread over the
+// slots, half HALF of the stage's global->LDS copies.  Spreading the copies
+// over both substeps keeps their issue rate below what the texture path
+// drains, so a wave never stalls on a full copy queue while its matrix core
+// idles.
+template <int FM, int FN, int NA, int NB, int BM, int HALF, int RS, bool AK, bool BK, int BN,
+          bool SW = false>
 __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
                                              const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
-                                             const uint16_t* pa, const uint16_t* pb,
-                                             const RingDma<NA * 64>& da,
-                                             const RingDma<NB * 64>& db, const uint16_t* oa,
-                                             const uint16_t* ob, uint16_t* dst, int wave_u) {
+                                             const RingOp<AK, BM>& ra, const uint16_t* ra_st,
+                                             const RingOp<BK, BN>& rb, const uint16_t* rb_st,
+                                             const uint16_t* oa, const uint16_t* ob, uint16_t* dst,
+                                             int wave_u) {
   constexpr int RA = BM * kRK;
   constexpr int H = (NA + NB) / 2;  // copies per substep
   static_assert((NA + NB) % 2 == 0, "copies split evenly over two substeps");
@@ -433,12 +473,12 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
     // (the MFMA is issued before the slot's reads, so the wait for its own
     // operands never covers the reads issued after it)
     __builtin_amdgcn_sched_barrier(0);
-    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kRK);
-    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kRK);
+    if (q < FM) na[q] = ra.template frag<RS>(ra_st, q);
+    else if (q < FM + FN) nb[q - FM] = rb.template frag<RS>(rb_st, q - FM);
     if (q % STEP == 0 && q / STEP < H) {
       const int n = HALF * H + q / STEP;
-      if (n < NA) da.issue_one(oa, dst, wave_u, n);
-      else db.issue_one(ob, dst + RA, wave_u, n - NA);
+      if (n < NA) ra.issue_one(oa, dst, wave_u, n);
+      else rb.issue_one(ob, dst + RA, wave_u, n - NA);
     }
     if constexpr (STEP == 1 && FM * FN < H) {
       // more copies than slots: issue the rest with the last slot
@@ -446,8 +486,8 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
 #pragma unroll
         for (int c = FM * FN; c < H; ++c) {
           const int n = HALF * H + c;
-          if (n < NA) da.issue_one(oa, dst, wave_u, n);
-          else db.issue_one(ob, dst + RA, wave_u, n - NA);
+          if (n < NA) ra.issue_one(oa, dst, wave_u, n);
+          else rb.issue_one(ob, dst + RA, wave_u, n - NA);
         }
       }
     }
@@ -456,7 +496,7 @@ __device__ __forceinline__ void ring_substep(f32x16_t (&acc)[FM][FN], const bf16
 }
 
 // k range [k0, k0 + nk * kRK).
-template <int BM, int BN, int FM, int FN, bool SW = false>
+template <int BM, int BN, int FM, int FN, bool AK, bool BK, bool SW = false>
 __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
                                               uint16_t* lds, int wave, int lane, int wm, int wn,
                                               f32x16_t (&acc)[FM][FN]) {
@@ -469,19 +509,13 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
   // first half of stage kt+S-1.
   constexpr int WAIT_FIRST = waitcnt_imm((NA + NB) * (S - 2), 0);
   constexpr int WAIT_NEXT = waitcnt_imm((NA + NB) * (S - 3) + (NA + NB) / 2, 0);
-  const int h = lane >> 5, lc = lane & 31;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  RingDma<BM> da;
-  RingDma<BN> db;
-  da.init(p.lda, wave, lane);
-  db.init(p.ldb, wave, lane);
-  const uint16_t* oa = p.A + (int64_t)m0 * p.lda + k0;
-  const uint16_t* ob = p.B + (int64_t)n0 * p.ldb + k0;
-  // fragment addressing inside a stage (elements)
-  const int a_off = (wm * (BM / 2) + lc) * kRK;
-  const int b_off = RA + (wn * (BN / 2) + lc) * kRK;
-  const int xo0 = ((0 + h) ^ rswz(lc)) << 3;  // substep 0: k 0..15 of the stage
-  const int xo1 = ((2 + h) ^ rswz(lc)) << 3;  // substep 1: k 16..31
+  RingOp<AK, BM> ra;
+  RingOp<BK, BN> rb;
+  ra.init(p.lda, wave, lane, wm);
+  rb.init(p.ldb, wave, lane, wn);
+  const uint16_t* oa = RingOp<AK, BM>::origin(p.A, p.lda, m0, k0);
+  const uint16_t* ob = RingOp<BK, BN>::origin(p.B, p.ldb, n0, k0);
 
   // Prologue: stages 0 .. S-2.  Stages past the end of K re-read stage 0
   // into slots that are never multiplied, which keeps the number of copies
@@ -489,20 +523,20 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
 #pragma unroll
   for (int g = 0; g < S - 1; ++g) {
     const int kk = (g < nk ? g : 0) * kRK;
+    const uint16_t* sa = oa + RingOp<AK, BM>::kstep(p.lda, kk);
+    const uint16_t* sb = ob + RingOp<BK, BN>::kstep(p.ldb, kk);
 #pragma unroll
-    for (int j = 0; j < NA; ++j) da.issue_one(oa + kk, lds + g * RST, wave_u, j);
+    for (int j = 0; j < NA; ++j) ra.issue_one(sa, lds + g * RST, wave_u, j);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) db.issue_one(ob + kk, lds + g * RST + RA, wave_u, j);
+    for (int j = 0; j < NB; ++j) rb.issue_one(sb, lds + g * RST + RA, wave_u, j);
   }
   __builtin_amdgcn_s_waitcnt(WAIT_FIRST);
   __builtin_amdgcn_s_barrier();
   bf16x8_t fa[2][FM], fb[2][FN];
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
-    fa[0][i] = *reinterpret_cast<const bf16x8_t*>(lds + a_off + xo0 + i * 32 * kRK);
+  for (int i = 0; i < FM; ++i) fa[0][i] = ra.template frag<0>(lds, i);
 #pragma unroll
-  for (int j = 0; j < FN; ++j)
-    fb[0][j] = *reinterpret_cast<const bf16x8_t*>(lds + b_off + xo0 + j * 32 * kRK);
+  for (int j = 0; j < FN; ++j) fb[0][j] = rb.template frag<0>(lds + RA, j);
 
   int cur = 0;
   for (int kt = 0; kt < nk; ++kt) {
@@ -510,11 +544,13 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
     const int slot = cur == 0 ? S - 1 : cur - 1;  // freed by stage kt-1
     const int kd = kt + S - 1;
     const int kk = (kd < nk ? kd : 0) * kRK;
+    const uint16_t* sa = oa + RingOp<AK, BM>::kstep(p.lda, kk);
+    const uint16_t* sb = ob + RingOp<BK, BN>::kstep(p.ldb, kk);
     const uint16_t* st = lds + cur * RST;
     __builtin_amdgcn_sched_barrier(0);
-    ring_substep<FM, FN, NA, NB, BM, 0, SW>(acc, fa[0], fb[0], fa[1], fb[1], st + a_off + xo1,
-                                            st + b_off + xo1, da, db, oa + kk, ob + kk,
-                                            lds + slot * RST, wave_u);
+    ring_substep<FM, FN, NA, NB, BM, 0, 1, AK, BK, BN, SW>(acc, fa[0], fb[0], fa[1], fb[1], ra, st,
+                                                          rb, st + RA, sa, sb, lds + slot * RST,
+                                                          wave_u);
     // Stage kt+1 landed (own copies: vmcnt; everyone's: the barrier), and
     // every wave finished reading stage kt (lgkmcnt), which the copies of
     // the next iteration overwrite.
@@ -522,9 +558,9 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     const uint16_t* sn = lds + nxt * RST;
-    ring_substep<FM, FN, NA, NB, BM, 1, SW>(acc, fa[1], fb[1], fa[0], fb[0], sn + a_off + xo0,
-                                            sn + b_off + xo0, da, db, oa + kk, ob + kk,
-                                            lds + slot * RST, wave_u);
+    ring_substep<FM, FN, NA, NB, BM, 1, 0, AK, BK, BN, SW>(acc, fa[1], fb[1], fa[0], fb[0], ra, sn,
+                                                          rb, sn + RA, sa, sb, lds + slot * RST,
+                                                          wave_u);
     cur = nxt;
   }
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));  // the trailing re-reads
@@ -790,13 +826,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
 
   const bool interior = aligned && m0 + BM <= p.M && n0 + BN <= p.N && (kbeg % kBK) == 0 &&
                         ((kend - kbeg) % kBK) == 0 && p.lda < (1 << 23) && p.ldb < (1 << 23);
-  if (A_KMAJOR && B_KMAJOR && interior && BM == 256) {
-    dma2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane, a_base,
-                                  b_base, xo, acc);
-  } else if (A_KMAJOR && B_KMAJOR && interior && BM == 128) {
-    ring_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kRK, lds, wave, lane, wm,
-                                      wn, acc);
-  } else {
+  bool staged = false;  // main loop done on a global->LDS copy path
+  if constexpr (A_KMAJOR && B_KMAJOR) {
+    if (interior && BM == 256) {
+      dma2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
+                                        a_base, b_base, xo, acc);
+      staged = true;
+    } else if (interior) {
+      ring_mainloop<BM, BN, FM, FN, A_KMAJOR, B_KMAJOR, SW>(p, m0, n0, kbeg, (kend - kbeg) / kRK,
+                                                            lds, wave, lane, wm, wn, acc);
+      staged = true;
+    }
+  }
+  if (!staged) {
     // General path: any layout, ragged edges, unaligned operands.  16-byte
     // (or masked element) loads into registers, one k-step ahead, then
     // (transposing if needed) stores into the other LDS stage.
