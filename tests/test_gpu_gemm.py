@@ -215,3 +215,21 @@ def test_streams_do_not_share_workspace():
         tgemm.set_split_k(prev)
     for i, C in enumerate(outs):
         assert torch.equal(C, serial[i % 2])
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("M,N,K", [(384, 200, 512), (200, 384, 512), (320, 320, 448), (520, 264, 192)])
+def test_ragged_k64_layouts_bitwise(M, N, K, cfg):
+    """Ragged shapes with K a multiple of 64 (interior tiles on the
+    global->LDS paths, edge tiles on the register path): every layout must
+    give the bits of TN (both operands MN-contiguous) and NT must match the
+    oracle."""
+    outs = {}
+    for ta, tb in LAYOUTS:
+        d = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K)
+        outs[ta + tb] = run_store(d, ta, tb, M, N, K, out_dtype=torch.float32, cfg=cfg)
+        if ta + tb == "NT":
+            ref = oracle_gemm_from(d, ta, tb, M, N, K)
+            assert scaled_err(outs["NT"].cpu().numpy(), ref) <= 1e-4
+    for k, v in outs.items():
+        assert torch.equal(v, outs["TN"]), k
