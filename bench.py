@@ -108,6 +108,43 @@ def cpu_baseline(budget_s=12.0):
                       f"explicit transpose + BLAS matmul), {t_total:.1f} s"}
 
 
+def cpu_oracle_secondary(budget_s=6.0):
+    """The oracle on bounded samples of the other workloads, for the
+    secondary figures: fused CE (whole rows of the 4096x32000x4096 logits,
+    then the per-row loss) and the K=1 RoPE table (4096 positions)."""
+    import numpy as np
+
+    import oracle
+    import workloads
+
+    out = {}
+    cv = workloads.ce_vocab()
+    Hb = workloads.bf16_bits(cv["H"]).reshape(-1)
+    Wb = workloads.bf16_bits(cv["W"]).reshape(-1)
+    lab = cv["labels"].numpy()
+    rows, t, n = np.arange(0, 8), 0.0, 0
+    while t < budget_s and n < 8:
+        r = rows + 8 * n
+        t0 = time.perf_counter()
+        logits = oracle.gemm("N", "T", 4096, 32000, 4096, Hb, 4096, Wb, 4096, rows=r)
+        oracle.cross_entropy(logits, lab[r])
+        t += time.perf_counter() - t0
+        n += 1
+    out["cpu_oracle_ce_rows_per_s"] = round(8 * n / t, 2)
+    out["cpu_oracle_ce_sample"] = f"{8 * n} rows of 4096x32000x4096 (fp64 logits + loss), {t:.1f} s"
+    r = workloads.rope()
+    pos, inv = r["pos"].numpy(), r["inv_freq"].numpy()
+    t0 = time.perf_counter()
+    reps = 0
+    while time.perf_counter() - t0 < 1.0:
+        oracle.rope_tables(pos, inv)
+        reps += 1
+    tr = time.perf_counter() - t0
+    out["cpu_oracle_rope_GBps"] = round(reps * (2 * 4096 * 128 * 2 + 4096 * 8) / tr / 1e9, 4)
+    out["cpu_oracle_rope_sample"] = f"{reps} x 4096-position table, {tr:.1f} s"
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -252,6 +289,8 @@ def main():
     if not args.no_cpu_baseline:
         log("timing the CPU oracle sample ...")
         out["cpu_baseline"] = cpu_baseline()
+        if not args.only_nt:
+            out["secondary"].update(cpu_oracle_secondary())
     print(json.dumps(out), flush=True)
     return 0
 
