@@ -235,7 +235,17 @@ def main():
         secondary["ce_loss_ms"] = round(ms_ce, 4)
         secondary["ce_grad_rows_per_s"] = round(Mc / (ms_ceg * 1e-3), 1)
         secondary["ce_grad_ms"] = round(ms_ceg, 4)
-        del Hs, Wv, g
+        # the GEMMs that consume the gradient, operands read as stored:
+        # dH = G . W (NN, K = 32000) and dW = G^T . H (TN, K = 4096)
+        dH = torch.empty(Mc, Kc, dtype=torch.bfloat16, device=dev)
+        dW = torch.empty(Nc, Kc, dtype=torch.bfloat16, device=dev)
+        ms_dh = time_stream(lambda i: tgemm.run("N", "N", Mc, Kc, Nc, g, Nc, Wv[0], Kc, dH, Kc,
+                                                tgemm.EPI_STORE_BF16), max(5, K_ // 5), 2, 1)
+        ms_dw = time_stream(lambda i: tgemm.run("T", "N", Nc, Kc, Mc, g, Nc, Hs[0], Kc, dW, Kc,
+                                                tgemm.EPI_STORE_BF16), max(5, K_ // 5), 2, 1)
+        secondary["ce_bwd_dH_NN_tflops"] = round(ce_fl / (ms_dh * 1e-3) / 1e12, 2)
+        secondary["ce_bwd_dW_TN_tflops"] = round(ce_fl / (ms_dw * 1e-3) / 1e12, 2)
+        del Hs, Wv, g, dH, dW
 
         # ---- layout sweep 4096^3 ------------------------------------------
         ls = workloads.layout_sweep()

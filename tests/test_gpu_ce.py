@@ -140,3 +140,31 @@ def test_ce_vocab_full_size():
     sums = g.float().sum(dim=1)
     assert sums.abs().max().item() <= 2.0 ** -7 + 1e-3
     assert (loss > 0).all().item()
+
+
+def test_ce_backward_gemms_full_size():
+    """The two GEMMs that consume the gradient G = softmax - onehot of the
+    fused CE, each reading its operands as stored: dH = G . W is an NN call
+    (W stored [32000, 4096] is op(B) as is), dW = G^T . H a TN call (G read
+    transposed in place).  Sampled rows against the oracle on the same bf16
+    bits of G."""
+    w = workloads.ce_vocab()
+    H, W, lab = w["H"].to(dev()), w["W"].to(dev()), w["labels"].to(dev())
+    M, N, K = 4096, 32000, 4096
+    _, G = tgemm.cross_entropy(H, W.t(), lab, grad=True)
+    dH = tgemm.matmul(G, W)            # [4096, 32000] . [32000, 4096]
+    dW = tgemm.matmul(G.t(), H)        # [32000, 4096] . [4096, 4096]
+    torch.cuda.synchronize()
+    assert tgemm.layout_of(G)[0] == "N" and tgemm.layout_of(W)[0] == "N"
+    assert tgemm.layout_of(G.t())[0] == "T" and tgemm.layout_of(H)[0] == "N"
+    Gb = bits(G).reshape(-1)
+    Wb = workloads.bf16_bits(w["W"]).reshape(-1)
+    Hb = workloads.bf16_bits(w["H"]).reshape(-1)
+    rows = sample_rows(M, 16, seed=6, tile=256)
+    ref = oracle.gemm("N", "N", M, K, N, Gb, N, Wb, K, rows=rows)
+    got = bf16_to_f64(dH[torch.as_tensor(rows, device=dev())])
+    assert scaled_err(got, ref) <= GEMM_BF16_TOL
+    rows = sample_rows(N, 16, seed=7, tile=256)
+    ref = oracle.gemm("T", "N", N, K, M, Gb, N, Hb, K, rows=rows)
+    got = bf16_to_f64(dW[torch.as_tensor(rows, device=dev())])
+    assert scaled_err(got, ref) <= GEMM_BF16_TOL
