@@ -204,6 +204,59 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
     return status_of(e);
   }
 
+  if ((M == 1 || N == 1) && K > 1 &&
+      (epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32)) {
+    // Matrix-vector or dot product: HBM-bound reductions, no matrix cores.
+    const uint16_t* a = static_cast<const uint16_t*>(A);
+    const uint16_t* b = static_cast<const uint16_t*>(B);
+    int shape = kGemvRows;
+    const uint16_t *X, *v;
+    int64_t ldx = 0, sx = 1, sv, sc;
+    int L;
+    if (M == 1 && N == 1) {
+      // dot product of op(A)[0, :] and op(B)[:, 0]; the unit-stride one is X
+      const int64_t sa2 = is_n(transA) ? 1 : lda, sb2 = is_n(transB) ? ldb : 1;
+      if (sa2 == 1 || sb2 != 1) {
+        X = a, sx = sa2, v = b, sv = sb2;
+      } else {
+        X = b, sx = sb2, v = a, sv = sa2;
+      }
+      L = 1;
+      sc = 1;
+    } else if (N == 1) {
+      // y[m] = op(A)[m, :] . op(B)[:, 0]
+      v = b;
+      sv = is_n(transB) ? ldb : 1;
+      X = a;
+      ldx = lda;
+      shape = is_n(transA) ? kGemvRows : kGemvCols;
+      L = m;
+      sc = ldc;
+    } else {
+      // y[n] = op(A)[0, :] . op(B)[:, n]
+      v = a;
+      sv = is_n(transA) ? 1 : lda;
+      X = b;
+      ldx = ldb;
+      shape = is_n(transB) ? kGemvCols : kGemvRows;
+      L = n;
+      sc = 1;
+    }
+    const int64_t nkc = gemv_chunks(shape, L, K);
+    if (nkc * L > (int64_t(1) << 31)) return TGEMM_ERR_UNSUPPORTED;
+    if (verbose())
+      fprintf(stderr, "tgemm: %s M=%d N=%d K=%lld L=%d chunks=%lld\n",
+              shape == kGemvRows ? "rowdot" : "colsweep", m, n, (long long)K, L, (long long)nkc);
+    Workspace w;
+    if (!get_workspace(s, (size_t)(nkc * L) * sizeof(float), &w)) return TGEMM_ERR_NO_MEMORY;
+    hipError_t e = launch_gemv(shape, X, ldx, sx, v, sv, L, K, (int)nkc,
+                               static_cast<float*>(w.ptr), C, sc,
+                               epilogue == TGEMM_EPI_STORE_F32, s);
+    const hipError_t ef = release_workspace(w, s);
+    if (e == hipSuccess) e = ef;
+    return status_of(e);
+  }
+
   int split = 1;
   const int cfg = choose_tile(is_n(transA) && !is_n(transB), m, n, k, epilogue, &split);
   GemmParams p = {};

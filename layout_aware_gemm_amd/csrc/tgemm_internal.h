@@ -51,6 +51,19 @@ hipError_t launch_gemm_tt(int cfg, int epi, const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_sum(const float* ws, int split, int M, int N, void* C, int64_t ldc,
                              bool out_f32, hipStream_t s);
 
+// Matrix-vector and dot products (M = 1 or N = 1, K > 1; defined in
+// gemv.hip).  The matrix operand X holds L output rows of K elements:
+// kGemvRows when each row is contiguous (row r at X + r*ldx, element k at
+// stride sx), kGemvCols when X is stored [K][L] (element (k, r) at
+// X + k*ldx + r).  v is the K-vector (stride sv).  gemv_chunks gives the
+// number of K chunks, whose fp32 partials [chunks][L] `partial` must hold;
+// the result r is stored at C + r*sc.
+enum GemvShape : int { kGemvRows = 0, kGemvCols = 1 };
+int64_t gemv_chunks(int shape, int L, int64_t K);
+hipError_t launch_gemv(int shape, const uint16_t* X, int64_t ldx, int64_t sx, const uint16_t* v,
+                       int64_t sv, int L, int64_t K, int nkc, float* partial, void* C,
+                       int64_t sc, bool out_f32, hipStream_t s);
+
 // Cross-entropy combine (per row: fold block partials in ascending block
 // order, loss = lse - y[label]) and gradient fix-up (defined in ce.hip).
 hipError_t launch_ce_combine(const float* part_m, const float* part_s, const float* ylabel,

@@ -98,7 +98,8 @@ def test_bf16_decode_exact():
 
 # ------------------------------------------------------------------- GEMM
 TINY = [(1, 1, 1), (3, 5, 7), (7, 3, 13), (13, 17, 2), (5, 9, 16), (17, 1, 9), (2, 16, 1),
-        (9, 4, 9), (6, 6, 6)]  # square cases catch a transpose swapped for a no-op
+        (9, 4, 9), (6, 6, 6),  # square cases catch a transpose swapped for a no-op
+        (1, 11, 14), (1, 1, 17)]  # a row vector times a matrix, a dot product
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
