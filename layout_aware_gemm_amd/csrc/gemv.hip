@@ -15,9 +15,10 @@
 //     takes 8 consecutive outputs and walks a K chunk, the element v[k] is
 //     the same for the whole workgroup.
 // Both write one fp32 partial per (K chunk, output) to the workspace;
-// combine then adds the chunks of each output in ascending chunk order --
-// a fixed order, so results do not depend on scheduling -- and stores
-// bf16 (round to nearest even) or fp32.
+// combine then adds the chunks of each output in a fixed order -- so
+// results do not depend on scheduling -- and stores bf16 (round to nearest
+// even) or fp32.  With a single chunk the reduction kernel stores the
+// output itself and no combine pass runs.
 #include "bf16_cvt.h"
 #include "tgemm_internal.h"
 
@@ -25,7 +26,13 @@ namespace tgemm {
 
 namespace {
 
-// partial[kc * L + r] = sum over k in chunk kc of X[r*ldx + k*sx] * v[k*sv].
+__device__ __forceinline__ void store_out(void* C, int64_t off, float s, int out_f32) {
+  if (out_f32) static_cast<float*>(C)[off] = s;
+  else static_cast<uint16_t*>(C)[off] = to_bf16(s);
+}
+
+// partial[kc * L + r] = sum over k in chunk kc of X[r*ldx + k*sx] * v[k*sv]
+// (with a single chunk the sum goes straight to the output C + r*sc).
 // Workgroup = 4 waves = 4 (row, chunk) items.  VEC: sx == sv == 1, rows and
 // v 16-byte aligned; lanes then take 8 consecutive k per step.
 template <bool VEC>
@@ -33,7 +40,8 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const uint16_t* __restrict_
                                                      int64_t sx, const uint16_t* __restrict__ v,
                                                      int64_t sv, int L, int64_t K,
                                                      int64_t kchunk, int nkc,
-                                                     float* __restrict__ partial) {
+                                                     float* __restrict__ partial, void* C,
+                                                     int64_t sc, int out_f32) {
   const int lane = threadIdx.x & 63;
   const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (item >= (int64_t)L * nkc) return;
@@ -76,7 +84,9 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const uint16_t* __restrict_
     acc = fmaf(from_bf16(x[k * sx]), from_bf16(v[k * sv]), acc);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o, 64);
-  if (lane == 0) partial[(int64_t)kc * L + r] = acc;
+  if (lane != 0) return;
+  if (nkc > 1) partial[(int64_t)kc * L + r] = acc;
+  else store_out(C, (int64_t)r * sc, acc, out_f32);  // one chunk: no combine pass
 }
 
 // partial[kc * L + c] = sum over k in chunk kc of X[k*ldx + c] * v[k*sv] for
@@ -85,7 +95,9 @@ template <bool VEC>
 __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restrict__ X,
                                                        int64_t ldx, const uint16_t* __restrict__ v,
                                                        int64_t sv, int L, int64_t K,
-                                                       int64_t kchunk, float* __restrict__ partial) {
+                                                       int64_t kchunk, int nkc,
+                                                       float* __restrict__ partial, void* C,
+                                                       int64_t sc, int out_f32) {
   const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
   const int kc = blockIdx.y;
   const int64_t k0 = (int64_t)kc * kchunk;
@@ -131,22 +143,31 @@ __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restric
       }
     }
 #pragma unroll
-    for (int e = 0; e < 8; ++e)
-      if (c0 + e < L) partial[(int64_t)kc * L + c0 + e] = acc[e];
+    for (int e = 0; e < 8; ++e) {
+      if (c0 + e >= L) continue;
+      if (nkc > 1) partial[(int64_t)kc * L + c0 + e] = acc[e];
+      else store_out(C, (int64_t)(c0 + e) * sc, acc[e], out_f32);
+    }
   }
 }
 
 // y[r] = sum over kc = 0, 1, ..., nkc-1 of partial[kc * L + r], stored at
-// C + r*sc.  One thread per output when few chunks; otherwise one
-// workgroup per output: thread t adds chunks t, t+256, ... in order, then
-// the 256 thread sums are folded pairwise in a fixed tree.
-template <bool BLOCK>
+// C + r*sc, in one of three fixed orders (each deterministic):
+//   MODE 0 (few chunks): one thread per output adds the chunks in order.
+//   MODE 1 (many chunks, many outputs): a workgroup takes 16 consecutive
+//     outputs and 16 chunk lanes; lane q adds chunks q, q+16, q+32, ...
+//     (the 16 threads of a lane read 16 consecutive partials), then the 16
+//     lane sums are added in ascending q.
+//   MODE 2 (many chunks, under 16 outputs): a workgroup per output; thread t
+//     adds chunks t, t+256, ..., then the 256 sums are folded pairwise in a
+//     fixed tree.
+template <int MODE>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partial, int L,
                                                       int nkc, void* __restrict__ C, int64_t sc,
                                                       int out_f32) {
   float s;
   int64_t r;
-  if constexpr (BLOCK) {
+  if constexpr (MODE == 2) {
     __shared__ float red[256];
     r = blockIdx.x;
     float t = 0.f;
@@ -159,14 +180,26 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     }
     if (threadIdx.x != 0) return;
     s = red[0];
+  } else if constexpr (MODE == 1) {
+    __shared__ float red[16][16];
+    const int j = threadIdx.x & 15, q = threadIdx.x >> 4;
+    r = (int64_t)blockIdx.x * 16 + j;
+    float t = 0.f;
+    if (r < L)
+      for (int kc = q; kc < nkc; kc += 16) t += partial[(int64_t)kc * L + r];
+    red[q][j] = t;
+    __syncthreads();
+    if (q != 0 || r >= L) return;
+    s = 0.f;
+#pragma unroll
+    for (int u = 0; u < 16; ++u) s += red[u][j];
   } else {
     r = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (r >= L) return;
     s = 0.f;
     for (int kc = 0; kc < nkc; ++kc) s += partial[(int64_t)kc * L + r];
   }
-  if (out_f32) static_cast<float*>(C)[r * sc] = s;
-  else static_cast<uint16_t*>(C)[r * sc] = to_bf16(s);
+  store_out(C, r * sc, s, out_f32);
 }
 
 inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -175,8 +208,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t gemv_chunks(int shape, int L, int64_t K) {
   if (shape == kGemvRows) {
-    // at least ~4096 waves in flight, chunks of at least 4096 elements
-    int64_t n = cdiv(4096, L);
+    // at least ~8192 waves, chunks of at least 4096 elements
+    int64_t n = cdiv(8192, L);
     const int64_t most = cdiv(K, 4096);
     if (n > most) n = most;
     return n < 1 ? 1 : n;
@@ -202,10 +235,10 @@ hipError_t launch_gemv(int shape, const uint16_t* X, int64_t ldx, int64_t sx, co
     const dim3 grid((unsigned)cdiv(items, 4));
     if (vec)
       hipLaunchKernelGGL(rowdot_kernel<true>, grid, dim3(256), 0, s, X, ldx, sx, v, sv, L, K,
-                         kchunk, nkc, partial);
+                         kchunk, nkc, partial, C, sc, out_f32 ? 1 : 0);
     else
       hipLaunchKernelGGL(rowdot_kernel<false>, grid, dim3(256), 0, s, X, ldx, sx, v, sv, L, K,
-                         kchunk, nkc, partial);
+                         kchunk, nkc, partial, C, sc, out_f32 ? 1 : 0);
   } else {
     const int64_t kchunk = cdiv(K, nkc);
     nkc = (int)cdiv(K, kchunk);
@@ -213,19 +246,23 @@ hipError_t launch_gemv(int shape, const uint16_t* X, int64_t ldx, int64_t sx, co
     const dim3 grid((unsigned)cdiv(L, 2048), (unsigned)nkc);
     if (vec)
       hipLaunchKernelGGL(colsweep_kernel<true>, grid, dim3(256), 0, s, X, ldx, v, sv, L, K, kchunk,
-                         partial);
+                         nkc, partial, C, sc, out_f32 ? 1 : 0);
     else
       hipLaunchKernelGGL(colsweep_kernel<false>, grid, dim3(256), 0, s, X, ldx, v, sv, L, K,
-                         kchunk, partial);
+                         kchunk, nkc, partial, C, sc, out_f32 ? 1 : 0);
   }
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (nkc > 32)
-    hipLaunchKernelGGL(combine_kernel<true>, dim3((unsigned)L), dim3(256), 0, s, partial, L, nkc,
-                       C, sc, out_f32 ? 1 : 0);
+  if (e != hipSuccess || nkc == 1) return e;
+  const int of = out_f32 ? 1 : 0;
+  if (nkc <= 16)
+    hipLaunchKernelGGL(combine_kernel<0>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, s, partial,
+                       L, nkc, C, sc, of);
+  else if (L >= 16)
+    hipLaunchKernelGGL(combine_kernel<1>, dim3((unsigned)cdiv(L, 16)), dim3(256), 0, s, partial, L,
+                       nkc, C, sc, of);
   else
-    hipLaunchKernelGGL(combine_kernel<false>, dim3((unsigned)cdiv(L, 256)), dim3(256), 0, s,
-                       partial, L, nkc, C, sc, out_f32 ? 1 : 0);
+    hipLaunchKernelGGL(combine_kernel<2>, dim3((unsigned)L), dim3(256), 0, s, partial, L, nkc, C,
+                       sc, of);
   return hipGetLastError();
 }
 
