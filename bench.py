@@ -260,6 +260,32 @@ def main():
             del A, B, C
         del ls
 
+        # ---- matrix-vector and dot products (M = 1 or N = 1) ---------------
+        wm = workloads.nt_mlp()
+        Wd = wm["W"].to(dev)                                  # [5120, 13824]
+        Wn = wm["W"].t().contiguous().to(dev)                 # [13824, 5120]
+        xd = wm["X"].reshape(-1, 13824)[:1].contiguous().to(dev)
+        del wm
+        yd = torch.empty(1, 5120, dtype=torch.bfloat16, device=dev)
+        gb = 5120 * 13824 * 2 + 13824 * 2 + 5120 * 2
+        for name, ta_, tb_, Bm, ldb_ in (("gemv_1x5120x13824_NT", "N", "T", Wd, 13824),
+                                          ("gemv_1x5120x13824_NN", "N", "N", Wn, 5120)):
+            msg = time_stream(lambda i: tgemm.run(ta_, tb_, 1, 5120, 13824, xd, 13824, Bm, ldb_, yd,
+                                                  5120, tgemm.EPI_STORE_BF16), K_, W_, 1)
+            secondary[f"{name}_us"] = round(msg * 1e3, 2)
+            secondary[f"{name}_frac_of_hbm"] = round(gb / (msg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        del Wd, Wn, xd, yd
+        Kd = 10 ** 8
+        gdot = torch.Generator(device="cpu").manual_seed(5)
+        av = torch.randn(Kd, generator=gdot).to(torch.bfloat16).to(dev)
+        bv = torch.randn(Kd, generator=gdot).to(torch.bfloat16).to(dev)
+        cd = torch.empty(1, 1, dtype=torch.float32, device=dev)
+        msd = time_stream(lambda i: tgemm.run("N", "N", 1, 1, Kd, av, Kd, bv, 1, cd, 1,
+                                              tgemm.EPI_STORE_F32), K_, W_, 1)
+        secondary["dot_1e8_us"] = round(msd * 1e3, 2)
+        secondary["dot_1e8_frac_of_hbm"] = round(4 * Kd / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        del av, bv, cd
+
         # ---- K=1 RoPE table --------------------------------------------------
         for name, r in (("rope_4096", workloads.rope()), ("rope_256x4096", workloads.rope_batched(256))):
             pos, inv = r["pos"].to(dev), r["inv_freq"].to(dev)
