@@ -208,8 +208,8 @@ inline int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 int64_t gemv_chunks(int shape, int L, int64_t K) {
   if (shape == kGemvRows) {
-    // at least ~8192 waves, chunks of at least 4096 elements
-    int64_t n = cdiv(8192, L);
+    // at least ~4096 waves, chunks of at least 4096 elements
+    int64_t n = cdiv(4096, L);
     const int64_t most = cdiv(K, 4096);
     if (n > most) n = most;
     return n < 1 ? 1 : n;
