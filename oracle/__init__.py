@@ -24,6 +24,11 @@ Everything is computed from the plain definitions in fp64 with NumPy:
                      (the %kernel_math listing and the proposed decomposition).
 * ``bf16``        -- exact bf16 decode and single-rounding round-to-nearest-
                      even encode.
+* ``e4m3_round`` / ``quantize`` / ``gemm_fp8``
+                  -- the fp8 cast of "Improve the Inductor generated kernel
+                     for the pattern of output1 = pointwise(input); output2 =
+                     transpose(output1)" (the example: scale, clamp, cast to
+                     e4m3fn) applied to both operands of the GEMM.
 
 Parity pins: every function is pinned in ``tests/test_oracle.py`` against
 brute force, closed forms, identities or library routines.  The exact bf16
@@ -35,6 +40,7 @@ from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
 from .gemm import op_matrix, gemm
 from .xent import cross_entropy, tile_partials, merge_partials, merge_pair
 from .rope import k1_outer, rope_tables
+from .fp8 import E4M3_MAX, e4m3_round, quantize, gemm_fp8
 
 __all__ = [
     "bf16_bits_to_f64",
@@ -47,4 +53,8 @@ __all__ = [
     "merge_pair",
     "k1_outer",
     "rope_tables",
+    "E4M3_MAX",
+    "e4m3_round",
+    "quantize",
+    "gemm_fp8",
 ]

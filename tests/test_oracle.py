@@ -346,3 +346,104 @@ def test_golden_page_shapes():
     assert [1, 1] + list(cos.shape) == r["outputs_T29_T31"]["shape"]
     assert [1, 1] + list(sin.shape) == r["outputs_T29_T31"]["shape"]
     assert list(workloads.rope()["inv_freq"].shape) == r["inv_freq_T3"]["shape"]
+
+
+# --------------------------------------------------------------- fp8 (e4m3fn)
+def torch_e4m3(y_f32):
+    """Library routine: torch's CPU cast to float8_e4m3fn and back."""
+    return torch.from_numpy(np.asarray(y_f32, dtype=np.float32)).to(torch.float8_e4m3fn).double().numpy()
+
+
+def all_e4m3_values():
+    codes = torch.arange(256, dtype=torch.int32).to(torch.uint8)
+    return codes.view(torch.float8_e4m3fn).double().numpy()
+
+
+def test_e4m3_grid_is_fixed_and_complete():
+    """Every finite e4m3fn value (decoded by torch from all 256 codes) is a
+    fixed point of the rounding; the set has 253 distinct finite values from
+    -448 to 448 and exactly two NaN codes."""
+    v = all_e4m3_values()
+    fin = v[np.isfinite(v)]
+    assert np.isnan(v).sum() == 2 and np.isinf(v).sum() == 0
+    assert len(np.unique(fin)) == 253 and fin.max() == 448.0 and fin.min() == -448.0
+    assert oracle.E4M3_MAX == 448.0
+    assert np.array_equal(oracle.e4m3_round(fin), fin)
+
+
+def test_e4m3_round_matches_library_cast_on_ties_and_random():
+    """Midpoints between neighbouring e4m3fn values (the ties), their fp32
+    neighbours, and random values in range: the oracle's rounding equals
+    torch's cast bit for bit (as values)."""
+    fin = np.unique(all_e4m3_values()[np.isfinite(all_e4m3_values())])
+    mids = ((fin[:-1] + fin[1:]) / 2).astype(np.float32)  # exact in fp32
+    ys = [fin.astype(np.float32), mids,
+          np.nextafter(mids, np.float32(np.inf)), np.nextafter(mids, np.float32(-np.inf))]
+    rng = np.random.default_rng(5)
+    ys += [(rng.standard_normal(20000) * 40).astype(np.float32),
+           (rng.standard_normal(5000) * 0.004).astype(np.float32)]
+    y = np.concatenate(ys)
+    y = y[np.abs(y) <= 448]
+    assert np.array_equal(oracle.e4m3_round(y), torch_e4m3(y))
+
+
+@pytest.mark.parametrize("x,expect", [
+    (1.0625, 1.0),            # halfway between 1 and 1.125: even fraction 000
+    (1.1875, 1.25),           # halfway between 1.125 and 1.25: even fraction 010
+    (2.0 ** -10, 0.0),        # half the smallest subnormal: ties to zero
+    (3 * 2.0 ** -10, 2.0 ** -8),  # 1.5 subnormal steps: ties to 2 steps
+    (2.0 ** -9, 2.0 ** -9),   # smallest subnormal
+    (0.0146484375, 0.015625),  # 7.5 * 2^-9: ties to 8 * 2^-9 = 2^-6, the smallest normal
+    (440.0, 448.0),           # 13.75 steps of 32 above 0: to 14
+    (-0.0, -0.0),
+])
+def test_e4m3_round_closed_forms(x, expect):
+    got = float(oracle.e4m3_round(np.float32(x)))
+    assert got == expect and math.copysign(1.0, got) == math.copysign(1.0, expect)
+
+
+def test_quantize_scale_clamp_nan():
+    """The page's cast: fp32 multiply, clamp to the largest finite value, round."""
+    x = np.array([1.0, 30.0, -50.0, 44.8, 0.3, np.nan, np.inf, -np.inf], dtype=np.float32)
+    q = oracle.quantize(x, 10.0)
+    # 300 rounds to 288 (spacing 32 above 256), -500 clamps, 44.8 * 10 rounds to 448
+    assert list(q[:5]) == [10.0, 288.0, -448.0, 448.0, 3.0]
+    assert np.isnan(q[5]) and q[6] == 448.0 and q[7] == -448.0
+    # the multiply rounds once in fp32 before the cast (0.1f * 3 is not 0.3)
+    s = np.float32(0.1)
+    y = np.float32(np.float32(3.0) * s)
+    assert oracle.quantize(np.float32(3.0), s) == torch_e4m3(y)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", [(3, 5, 7), (9, 4, 9), (1, 6, 11), (5, 1, 4)])
+def test_gemm_fp8_brute_force(ta, tb, M, N, K):
+    """Triple loop with each operand element cast by torch (the library
+    routine), against the oracle; scales and an output scale included."""
+    A, lda, B, ldb, _ = case(M, N, K, ta, tb, seed=M * 77 + N * 7 + K, pad=2, std=100.0)
+    sa, sb, so = 0.7, 3.0, 0.125
+    got = oracle.gemm_fp8(ta, tb, M, N, K, A, lda, B, ldb, sa, sb, so)
+
+    def qv(v, s):
+        y = np.clip(np.float32(v) * np.float32(s), -448, 448).astype(np.float32)
+        return float(torch_e4m3(np.array([y]))[0])
+
+    ref = np.zeros((M, N))
+    for m in range(M):
+        for n in range(N):
+            terms = []
+            for k in range(K):
+                a = stored_elem(A, lda, m, k) if ta == "N" else stored_elem(A, lda, k, m)
+                b = stored_elem(B, ldb, k, n) if tb == "N" else stored_elem(B, ldb, n, k)
+                terms.append(qv(a, sa) * qv(b, sb))
+            ref[m, n] = math.fsum(terms) * so
+    assert np.array_equal(got, ref)
+
+
+def test_gemm_fp8_reduces_to_gemm_on_small_integers():
+    """Integers in [-8, 8] are e4m3fn values: with unit scales the fp8 GEMM is
+    the bf16 GEMM exactly (a special case that reduces to the plain oracle)."""
+    for ta, tb in LAYOUTS:
+        A, lda, B, ldb, _ = case(40, 24, 70, ta, tb, seed=3, int_range=8)
+        assert np.array_equal(oracle.gemm_fp8(ta, tb, 40, 24, 70, A, lda, B, ldb, 1.0, 1.0),
+                              oracle.gemm(ta, tb, 40, 24, 70, A, lda, B, ldb))
