@@ -140,6 +140,47 @@ TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int
                    const int32_t* labels, const float* out_loss,
                    const void* out_grad);
 
+/*
+ * GEMM on fp8 (e4m3fn) operands made on the fly from bf16 inputs.
+ *
+ * ("Improve the Inductor generated kernel for the pattern of output1 =
+ * pointwise(input); output2 = transpose(output1)", the example: before a
+ * float8 linear each input element is scaled, clamped to the largest
+ * finite e4m3fn value and cast to e4m3fn, and the page's pattern also
+ * writes a transposed copy of the fp8 tensor.  Here the GEMM's loader
+ * applies the scale, clamp and cast to each element as it reads the bf16
+ * operand in its stored layout: no fp8 tensor and no transposed copy is
+ * ever written.)
+ *
+ *   transA, transB, M, N, K, A, lda, B, ldb, C, ldc: as for tgemm_run with
+ *                   a STORE epilogue; A and B are bf16 in any layout.
+ *   epilogue        TGEMM_EPI_STORE_BF16 or TGEMM_EPI_STORE_F32 only.
+ *   scales          device pointer to three fp32 values
+ *                   {scale_a, scale_b, out_scale}, read by the kernel.
+ *
+ * Each element x of op(A) becomes q = e4m3fn(clamp(fp32(x) * scale_a,
+ * -448, 448)): one fp32 multiply, the clamp (NaN stays NaN), then rounding
+ * to nearest e4m3fn value with ties to even; likewise op(B) with scale_b.
+ * C = out_scale * sum_k qA[m,k] * qB[k,n], products exact, fp32
+ * accumulation, one fp32 multiply by out_scale, then the store epilogue
+ * (bf16 with round-to-nearest-even, or fp32).  Pass out_scale =
+ * 1 / (scale_a * scale_b) to undo both casts.  The products run on the
+ * bf16 matrix cores, which hold every e4m3fn value exactly.
+ *
+ * Validation, errors, asynchrony and streams as for tgemm_run.  Needs no
+ * workspace.  Returns TGEMM_OK or a negative tgemm_status; an unsupported
+ * epilogue or a NULL `scales` is TGEMM_ERR_INVALID_ARG.
+ */
+TGEMM_API int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  void* C, int64_t ldc, int epilogue, const float* scales,
+                  void* stream);
+
+/* Host-only argument check of tgemm_run_fp8 (no GPU access). */
+TGEMM_API int tgemm_validate_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                  const void* C, int64_t ldc, int epilogue, const float* scales);
+
 /* Human-readable name of a status code (static string, never NULL). */
 TGEMM_API const char* tgemm_status_string(int status);
 

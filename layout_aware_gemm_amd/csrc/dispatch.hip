@@ -334,3 +334,44 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   if (e == hipSuccess) e = ef;
   return status_of(e);
 }
+
+// fp8 (e4m3fn) operands cast on load: every shape runs on the GEMM kernel's
+// register path (the direct copies would move raw bf16); no K split, no
+// matrix-vector or K = 1 shortcut, so every element goes through the cast.
+extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                             const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                             int64_t ldc, int epilogue, const float* scales, void* stream) {
+  const int st = tgemm_validate_fp8(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue,
+                                    scales);
+  if (st != TGEMM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
+  int cfg = g_forced_tile;
+  if (cfg == kTileAuto) cfg = t256 >= 200 ? kTile256 : kTile128;
+  if (cfg == kTilePP) cfg = kTile256;
+  GemmParams p = {};
+  p.A = static_cast<const uint16_t*>(A);
+  p.B = static_cast<const uint16_t*>(B);
+  p.lda = lda;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tilesM = ceil_div(M, tile_rows(cfg));
+  p.tilesN = ceil_div(N, tile_cols(cfg));
+  p.splitk = 1;
+  p.kchunk = (int)K;
+  if ((int64_t)p.tilesM * p.tilesN > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
+  p.groupM = p.tilesM < 4 ? p.tilesM : (p.tilesM <= 8 ? p.tilesM : 4);
+  p.aligned = ((reinterpret_cast<uintptr_t>(A) | reinterpret_cast<uintptr_t>(B)) & 15) == 0 &&
+              lda % 8 == 0 && ldb % 8 == 0;
+  p.C = C;
+  p.qscales = scales;
+  if (verbose())
+    fprintf(stderr, "tgemm: fp8 gemm %c%c M=%lld N=%lld K=%lld tile=%d grid=%dx%d aligned=%d\n",
+            transA, transB, (long long)M, (long long)N, (long long)K, cfg, p.tilesM, p.tilesN,
+            p.aligned);
+  return status_of(launch_gemm(transA, transB, cfg,
+                               epilogue == TGEMM_EPI_STORE_BF16 ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
+}

@@ -49,6 +49,46 @@ __device__ __forceinline__ uint32_t u4comp(const uint4& v, int d) {
 }
 
 // ----------------------------------------------------------------------
+// fp8 (e4m3fn) operands made on load ("Improve the Inductor generated
+// kernel for the pattern of output1 = pointwise(input); output2 =
+// transpose(output1)", the example: scale, clamp to the largest finite
+// e4m3fn value, cast).  Two bf16 values: fp32(x) * s (one rounding), clamp
+// to [-448, 448] with NaN kept, then v_cvt_pk_fp8_f32, whose rounding on
+// gfx950 is the OCP e4m3fn one (nearest, ties to even; it would turn a
+// magnitude past 448 into NaN, hence the clamp).  The e4m3fn values go back
+// to bf16, which holds each of them exactly, so the bf16 matrix cores
+// multiply the fp8 operands exactly.
+// ----------------------------------------------------------------------
+constexpr float kE4m3Max = 448.0f;
+
+__device__ __forceinline__ float clamp_e4m3(float y) {
+  const float c = fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
+  return y != y ? y : c;
+}
+
+__device__ __forceinline__ uint32_t q8_bf16x2(uint32_t w, float s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const float lo = clamp_e4m3(__fmul_rn(__uint_as_float(w << 16), s));
+  const float hi = clamp_e4m3(__fmul_rn(__uint_as_float(w & 0xffff0000u), s));
+  const int f8 = __builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
+  const float blo = __builtin_amdgcn_cvt_f32_fp8(f8, 0);
+  const float bhi = __builtin_amdgcn_cvt_f32_fp8(f8, 1);
+  // (an e4m3fn value has at most 4 significant bits: the low half is zero)
+  return (__float_as_uint(blo) >> 16) | (__float_as_uint(bhi) & 0xffff0000u);
+#else
+  (void)s;
+  return w;
+#endif
+}
+
+__device__ __forceinline__ void q8_vec(uint4& v, float s) {
+  v.x = q8_bf16x2(v.x, s);
+  v.y = q8_bf16x2(v.y, s);
+  v.z = q8_bf16x2(v.z, s);
+  v.w = q8_bf16x2(v.w, s);
+}
+
+// ----------------------------------------------------------------------
 // Operand loaders.  R = rows of the panel (M or N extent of the tile).
 // ----------------------------------------------------------------------
 
@@ -78,6 +118,12 @@ struct LoaderKMajor {
         v[i] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
+  }
+
+  // cast every loaded element to e4m3fn (Q8 epilogues); zero fill stays 0
+  __device__ __forceinline__ void quantize(float sc) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) q8_vec(v[i], sc);
   }
 
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
@@ -123,6 +169,11 @@ struct LoaderMNMajor {
         v[j] = make_uint4(w[0], w[1], w[2], w[3]);
       }
     }
+  }
+
+  __device__ __forceinline__ void quantize(float sc) {
+#pragma unroll
+    for (int j = 0; j < L; ++j) q8_vec(v[j], sc);
   }
 
   __device__ __forceinline__ uint32_t elem(int j, int i) const {
@@ -589,7 +640,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
                                          int n0, int wr0, int wc0, int pcol, uint16_t* lds,
                                          int tid, int lane) {
   const int h = lane >> 5, lc = lane & 31;
-  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32) {
+  constexpr bool Q8 = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32;
+  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32 || Q8) {
+    // (Q8: the sum times the output scale, one fp32 multiply)
+    float os = 1.f;
+    if constexpr (Q8) os = p.qscales[2];
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -599,11 +654,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wr0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
           if (row < p.M && col < p.N) {
-            if constexpr (EPI == kEpiStoreBf16)
-              reinterpret_cast<uint16_t*>(p.C)[(int64_t)row * p.ldc + col] =
-                  to_bf16(acc[i][j][r]);
+            float v = acc[i][j][r];
+            if constexpr (Q8) v = __fmul_rn(v, os);
+            if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16)
+              reinterpret_cast<uint16_t*>(p.C)[(int64_t)row * p.ldc + col] = to_bf16(v);
             else
-              reinterpret_cast<float*>(p.C)[(int64_t)row * p.ldc + col] = acc[i][j][r];
+              reinterpret_cast<float*>(p.C)[(int64_t)row * p.ldc + col] = v;
           }
         }
       }
@@ -826,7 +882,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr int SA = BM * kBK, SB = BN * kBK, STAGE = SA + SB;
   constexpr int RING = (BM + BN) * kRK * ring_stages<BM, BN>();
   constexpr bool SW = EPI == kEpiCE;  // transposed accumulators for row reductions
-  constexpr int LDS_ELEMS = (A_KMAJOR && B_KMAJOR && RING > 2 * STAGE) ? RING : 2 * STAGE;
+  constexpr bool Q8 = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32;  // e4m3fn operands made on load
+  constexpr int LDS_ELEMS =
+      (A_KMAJOR && B_KMAJOR && !Q8 && RING > 2 * STAGE) ? RING : 2 * STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
 
   const int tid = threadIdx.x;
@@ -862,7 +920,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   const bool interior = aligned && m0 + BM <= p.M && n0 + BN <= p.N && (kbeg % kBK) == 0 &&
                         ((kend - kbeg) % kBK) == 0 && p.lda < (1 << 23) && p.ldb < (1 << 23);
   bool staged = false;  // main loop done on a global->LDS copy path
-  if constexpr (A_KMAJOR && B_KMAJOR) {
+  // (the direct copies move raw bf16, so Q8 operands take the register path)
+  if constexpr (A_KMAJOR && B_KMAJOR && !Q8) {
     if (interior && BM == 256) {
       dma2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
                                         a_base, b_base, xo, acc);
@@ -882,6 +941,13 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     const int nk = (kend - kbeg + kBK - 1) / kBK;
     la.load(p.A, p.lda, m0, p.M, kbeg, kend, aligned, tid);
     lb.load(p.B, p.ldb, n0, p.N, kbeg, kend, aligned, tid);
+    float qa = 0.f, qb = 0.f;
+    if constexpr (Q8) {
+      qa = p.qscales[0];
+      qb = p.qscales[1];
+      la.quantize(qa);
+      lb.quantize(qb);
+    }
     la.store(lds, tid);
     lb.store(lds + SA, tid);
     __syncthreads();
@@ -901,6 +967,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       }
       if (more) {
         uint16_t* nx = lds + (cur ^ 1) * STAGE;
+        if constexpr (Q8) {
+          la.quantize(qa);
+          lb.quantize(qb);
+        }
         la.store(nx, tid);
         lb.store(nx + SA, tid);
       }
@@ -909,7 +979,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
 
   __syncthreads();  // every wave is done with LDS (the CE epilogue reuses it)
-  if constexpr (EPI != kEpiCE) {
+  if constexpr (EPI != kEpiCE && !Q8) {
     if (p.splitk > 1) {
       // K chunk ks of a split product: its fp32 partial goes to slice ks of
       // the workspace; a second kernel adds the slices in chunk order.
@@ -935,6 +1005,12 @@ hipError_t launch_gemm_tpl(int epi, const GemmParams& p, hipStream_t s) {
       break;
     case kEpiStoreF32:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiStoreF32>), grid, block, 0, s, p);
+      break;
+    case kEpiQ8Bf16:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiQ8Bf16>), grid, block, 0, s, p);
+      break;
+    case kEpiQ8F32:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiQ8F32>), grid, block, 0, s, p);
       break;
     default:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiCE>), grid, block, 0, s, p);

@@ -7,8 +7,16 @@
 
 namespace tgemm {
 
-// Epilogue variants of the matrix-core GEMM kernel.
-enum EpiKind : int { kEpiStoreBf16 = 0, kEpiStoreF32 = 1, kEpiCE = 2 };
+// Epilogue variants of the matrix-core GEMM kernel.  The Q8 stores take
+// operands cast to e4m3fn on load (scale, clamp, round) and multiply the
+// sum by the output scale before storing.
+enum EpiKind : int {
+  kEpiStoreBf16 = 0,
+  kEpiStoreF32 = 1,
+  kEpiCE = 2,
+  kEpiQ8Bf16 = 3,
+  kEpiQ8F32 = 4
+};
 
 // Tile configurations of the GEMM kernels (k-step 64):
 //   kTile256 / kTile128: BM x BN = 256x256 / 128x128, 4 waves in a 2x2 grid;
@@ -33,6 +41,8 @@ struct GemmParams {
   float* part_s;      // [nColBlocks][M] block sum of exp(y - block max)
   float* ylabel;      // [M] logit at the label column
   uint16_t* grad;     // optional [M][ldc] bf16: exp(y - block max), fixed up later
+  // Q8 epilogues: device fp32 {scale_a, scale_b, out_scale}
+  const float* qscales;
 };
 
 // Width (in columns) of the per-row partial blocks the CE epilogue writes.

@@ -58,6 +58,17 @@ extern "C" int tgemm_validate(char transA, char transB, int64_t M, int64_t N, in
   return TGEMM_OK;
 }
 
+extern "C" int tgemm_validate_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                  const void* A, int64_t lda, const void* B, int64_t ldb,
+                                  const void* C, int64_t ldc, int epilogue,
+                                  const float* scales) {
+  if (epilogue != TGEMM_EPI_STORE_BF16 && epilogue != TGEMM_EPI_STORE_F32)
+    return TGEMM_ERR_INVALID_ARG;
+  if (scales == nullptr) return TGEMM_ERR_INVALID_ARG;
+  return tgemm_validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, nullptr,
+                        nullptr, nullptr);
+}
+
 extern "C" const char* tgemm_status_string(int status) {
   switch (status) {
     case TGEMM_OK: return "TGEMM_OK";

@@ -29,8 +29,8 @@ EPI_CE = 2
 EPI_OUTER_F32 = 3
 EPI_ROPE_COSSIN = 4
 
-EXPORTS = ("tgemm_run", "tgemm_validate", "tgemm_status_string", "tgemm_set_tile_config",
-           "tgemm_set_split_k", "tgemm_version")
+EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
+           "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k", "tgemm_version")
 
 
 class TgemmError(RuntimeError):
@@ -59,6 +59,12 @@ def lib():
         L.tgemm_validate.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64, vp, i64, vp,
                                      i64, vp, i64, ctypes.c_int, vp, vp, vp]
         L.tgemm_validate.restype = ctypes.c_int
+        L.tgemm_run_fp8.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64, vp, i64, vp,
+                                    i64, vp, i64, ctypes.c_int, vp, vp]
+        L.tgemm_run_fp8.restype = ctypes.c_int
+        L.tgemm_validate_fp8.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64, vp, i64, vp,
+                                         i64, vp, i64, ctypes.c_int, vp]
+        L.tgemm_validate_fp8.restype = ctypes.c_int
         L.tgemm_status_string.argtypes = [ctypes.c_int]
         L.tgemm_status_string.restype = ctypes.c_char_p
         L.tgemm_set_tile_config.argtypes = [ctypes.c_int]
@@ -114,6 +120,27 @@ def validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue,
     return lib().tgemm_validate(_flag(transA), _flag(transB), int(M), int(N), int(K), _ptr(A),
                                 int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc), int(epilogue),
                                 _ptr(labels), _ptr(out_loss), _ptr(out_grad))
+
+
+def run_fp8(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, scales, stream=None,
+            check=True):
+    """Call ``tgemm_run_fp8``: bf16 operands cast to e4m3fn as they are
+    loaded; ``scales`` is a device fp32 [3] tensor {scale_a, scale_b,
+    out_scale} (or its address)."""
+    dev = A.device if isinstance(A, torch.Tensor) and A.is_cuda else None
+    st = lib().tgemm_run_fp8(_flag(transA), _flag(transB), int(M), int(N), int(K), _ptr(A),
+                             int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc), int(epilogue),
+                             _ptr(scales), _stream(stream, dev))
+    if check and st != TGEMM_OK:
+        raise TgemmError(st)
+    return st
+
+
+def validate_fp8(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, scales):
+    """Host-only ``tgemm_validate_fp8`` (no GPU needed)."""
+    return lib().tgemm_validate_fp8(_flag(transA), _flag(transB), int(M), int(N), int(K),
+                                    _ptr(A), int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc),
+                                    int(epilogue), _ptr(scales))
 
 
 def set_tile_config(cfg):
@@ -191,6 +218,35 @@ def matmul(a, b, out=None, out_dtype=torch.bfloat16, stream=None):
     if out.dtype not in (torch.bfloat16, torch.float32):
         raise TypeError("out must be bf16 or fp32")
     run(ta, tb, M, N, K, a2, lda, b, ldb, out, out.stride(0), epi, stream=stream)
+    return out.view(*lead, N)
+
+
+def matmul_fp8(a, b, scales, out=None, out_dtype=torch.bfloat16, stream=None):
+    """out_scale * (e4m3(a * scale_a) @ e4m3(b * scale_b)) for bf16 a [..., K]
+    and b [K, N] in any row/column-major view; ``scales`` is a device fp32
+    tensor {scale_a, scale_b, out_scale}.  No fp8 copy of either operand is
+    made, in either layout."""
+    lead = a.shape[:-1]
+    a2 = _flatten_rows(a)
+    if a2.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("matmul_fp8 expects bf16 operands")
+    if scales.dtype != torch.float32 or scales.numel() != 3 or not scales.is_contiguous():
+        raise ValueError("scales must be a contiguous fp32 tensor of 3 values")
+    M, K = a2.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    _check_dev(a2, b, scales)
+    ta, lda = layout_of(a2)
+    tb, ldb = layout_of(b)
+    if out is None:
+        out = torch.empty(M, N, dtype=out_dtype, device=a.device)
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape != (M, N):
+        raise ValueError("out must be a row-major [M, N] tensor")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise TypeError("out must be bf16 or fp32")
+    epi = EPI_STORE_BF16 if out.dtype == torch.bfloat16 else EPI_STORE_F32
+    run_fp8(ta, tb, M, N, K, a2, lda, b, ldb, out, out.stride(0), epi, scales, stream=stream)
     return out.view(*lead, N)
 
 

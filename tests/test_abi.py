@@ -123,3 +123,20 @@ def test_binding_refuses_cpu_tensors():
     a = torch.zeros(4, 4, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         tgemm.matmul(a, a)
+
+
+def test_validate_fp8_rules():
+    """fp8 calls: store epilogues only, scales required, else the bf16 rules."""
+    ok = dict(transA="N", transB="T", M=64, N=32, K=48, A=16, lda=48, B=16, ldb=48, C=16, ldc=32,
+              epilogue=tgemm.EPI_STORE_BF16, scales=16)
+    assert tgemm.validate_fp8(**ok) == tgemm.TGEMM_OK
+    assert tgemm.validate_fp8(**{**ok, "epilogue": tgemm.EPI_STORE_F32}) == tgemm.TGEMM_OK
+    for bad in ({"epilogue": tgemm.EPI_CE}, {"epilogue": 4}, {"scales": None},
+                {"lda": 47}, {"C": None}, {"K": 0}, {"transA": "X"}):
+        assert tgemm.validate_fp8(**{**ok, **bad}) == tgemm.TGEMM_ERR_INVALID_ARG, bad
+
+
+def test_run_fp8_rejects_before_touching_the_gpu():
+    st = tgemm.run_fp8("N", "T", 64, 32, 48, 16, 48, 16, 48, 16, 32, tgemm.EPI_CE, 16, stream=0,
+                       check=False)
+    assert st == tgemm.TGEMM_ERR_INVALID_ARG

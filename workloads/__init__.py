@@ -23,6 +23,13 @@ Workloads (shapes and distributions of the pages' examples):
                    "Schedule a small matmul op as a reduction (or pointwise)
                    op" (its fusion inputs)                          deterministic
 * ``rope_batched`` the same table for ``batch`` sequences of 0..4095
+* ``fp8_linear``   X bf16[4096,4096] N(0,1), W bf16[3072,4096] N(0,0.02) with
+                   the cast scales {10, 1000} -- the float8 linear of "Improve
+                   the Inductor generated kernel for the pattern of output1 =
+                   pointwise(input); output2 = transpose(output1)" (the
+                   example's M, K, N = 4096, 4096, 3072 and its input scale
+                   10; the weight's scale puts its values in the e4m3fn
+                   range the same way)                               seed 1005
 """
 
 import math
@@ -30,7 +37,8 @@ import math
 import numpy as np
 import torch
 
-SEEDS = {"tiny_ce": 1001, "nt_mlp": 1002, "layout_sweep": 1003, "ce_vocab": 1004}
+SEEDS = {"tiny_ce": 1001, "nt_mlp": 1002, "layout_sweep": 1003, "ce_vocab": 1004,
+         "fp8_linear": 1005}
 
 
 def _gen(seed):
@@ -112,6 +120,13 @@ def rope(seq=4096, dim=128):
 def rope_batched(batch=256, seq=4096, dim=128):
     pos = torch.arange(seq, dtype=torch.int64).repeat(batch)
     return {"pos": pos, "inv_freq": inv_freq(dim)}
+
+
+def fp8_linear(seed=SEEDS["fp8_linear"], M=4096, K=4096, N=3072):
+    g = _gen(seed)
+    x = randn_bf16((M, K), 1.0, g)
+    w = randn_bf16((N, K), 0.02, g)
+    return {"X": x, "W": w, "scale_x": 10.0, "scale_w": 1000.0}
 
 
 def random_operands(M, N, K, transA, transB, seed, std=1.0, pad=0, int_range=None):
