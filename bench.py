@@ -286,6 +286,37 @@ def main():
         secondary["dot_1e8_frac_of_hbm"] = round(4 * Kd / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         del av, bv, cd
 
+        # ---- fp8 (e4m3fn) operands cast on load: the float8 linear ----------
+        wf = workloads.fp8_linear()
+        Xf, Wf = wf["X"].to(dev), wf["W"].to(dev)              # [4096, 4096], [3072, 4096]
+        Wft = wf["W"].t().contiguous().to(dev)                 # [4096, 3072]
+        sx, sw = wf["scale_x"], wf["scale_w"]
+        sc = torch.tensor([sx, sw, 1.0 / (sx * sw)], dtype=torch.float32, device=dev)
+        del wf
+        Yf = torch.empty(4096, 3072, dtype=torch.bfloat16, device=dev)
+        f8fl = 2.0 * 4096 * 3072 * 4096
+        for name, tb_, Bm, ldb_ in (("fp8_linear_4096x3072x4096_NT", "T", Wf, 4096),
+                                    ("fp8_linear_4096x3072x4096_NN", "N", Wft, 3072)):
+            msf = time_stream(lambda i: tgemm.run_fp8("N", tb_, 4096, 3072, 4096, Xf, 4096, Bm,
+                                                      ldb_, Yf, 3072, tgemm.EPI_STORE_BF16, sc),
+                              K_, W_, 1)
+            secondary[f"{name}_us"] = round(msf * 1e3, 2)
+            secondary[f"{name}_tflops"] = round(f8fl / (msf * 1e-3) / 1e12, 2)
+            # the products run on the bf16 matrix cores
+            secondary[f"{name}_frac_of_bf16_peak"] = round(
+                f8fl / (msf * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
+        # context: the page's unfused pattern (scale, clamp and cast, then the
+        # transposed fp8 copy) for the input alone, in torch, before any GEMM
+        sxt = sc[0:1]
+
+        def unfused_cast(i):
+            t = (Xf * sxt).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+            return t.t().contiguous().t()
+
+        msu = time_stream(unfused_cast, K_, W_, 1)
+        secondary["fp8_cast_and_transposed_copy_torch_us"] = round(msu * 1e3, 2)
+        del Xf, Wf, Wft, Yf, sc
+
         # ---- K=1 RoPE table --------------------------------------------------
         for name, r in (("rope_4096", workloads.rope()), ("rope_256x4096", workloads.rope_batched(256))):
             pos, inv = r["pos"].to(dev), r["inv_freq"].to(dev)

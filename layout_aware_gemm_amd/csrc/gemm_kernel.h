@@ -54,38 +54,54 @@ __device__ __forceinline__ uint32_t u4comp(const uint4& v, int d) {
 // transpose(output1)", the example: scale, clamp to the largest finite
 // e4m3fn value, cast).  Two bf16 values: fp32(x) * s (one rounding), clamp
 // to [-448, 448] with NaN kept, then v_cvt_pk_fp8_f32, whose rounding on
-// gfx950 is the OCP e4m3fn one (nearest, ties to even; it would turn a
-// magnitude past 448 into NaN, hence the clamp).  The e4m3fn values go back
-// to bf16, which holds each of them exactly, so the bf16 matrix cores
-// multiply the fp8 operands exactly.
+// gfx950 is the OCP e4m3fn one (nearest, ties to even; it turns a
+// magnitude that rounds past 448 into NaN, hence the clamp, and its scaled
+// form only scales by powers of two).  The e4m3fn values go back to bf16,
+// which holds each of them exactly, so the bf16 matrix cores multiply the
+// fp8 operands exactly.
 // ----------------------------------------------------------------------
 constexpr float kE4m3Max = 448.0f;
 
-__device__ __forceinline__ float clamp_e4m3(float y) {
-  const float c = fminf(fmaxf(y, -kE4m3Max), kE4m3Max);
-  return y != y ? y : c;
-}
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
-__device__ __forceinline__ uint32_t q8_bf16x2(uint32_t w, float s) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  const float lo = clamp_e4m3(__fmul_rn(__uint_as_float(w << 16), s));
-  const float hi = clamp_e4m3(__fmul_rn(__uint_as_float(w & 0xffff0000u), s));
-  const int f8 = __builtin_amdgcn_cvt_pk_fp8_f32(lo, hi, 0, false);
-  const float blo = __builtin_amdgcn_cvt_f32_fp8(f8, 0);
-  const float bhi = __builtin_amdgcn_cvt_f32_fp8(f8, 1);
-  // (an e4m3fn value has at most 4 significant bits: the low half is zero)
-  return (__float_as_uint(blo) >> 16) | (__float_as_uint(bhi) & 0xffff0000u);
-#else
-  (void)s;
-  return w;
-#endif
+// fp32(bf16) * s, clamped to [-448, 448] by the IEEE 754-2019 minimum and
+// maximum (v_minimum3 / v_maximum3), which keep a NaN a NaN
+__device__ __forceinline__ float q8_scaled(uint32_t bf16_in_high_half, float s) {
+  const float y = __fmul_rn(__uint_as_float(bf16_in_high_half), s);
+  return __builtin_elementwise_minimum(__builtin_elementwise_maximum(y, -kE4m3Max), kE4m3Max);
 }
 
+// the high halves of two fp32 values (exact: an e4m3fn value has at most 4
+// significant bits) as a bf16 pair
+__device__ __forceinline__ uint32_t hi_halves(f32x2_t f) {
+  return __builtin_amdgcn_perm(__float_as_uint(f.y), __float_as_uint(f.x), 0x07060302u);
+}
+#endif
+
+// Cast the 8 bf16 values of one loaded 16-byte vector: two packed
+// conversions fill one register with four e4m3fn codes, and each register
+// converts back as two pairs.
 __device__ __forceinline__ void q8_vec(uint4& v, float s) {
-  v.x = q8_bf16x2(v.x, s);
-  v.y = q8_bf16x2(v.y, s);
-  v.z = q8_bf16x2(v.z, s);
-  v.w = q8_bf16x2(v.w, s);
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  int c[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t a = w[2 * h], b = w[2 * h + 1];
+    // (the first conversion's other half is overwritten by the second)
+    const int t = __builtin_amdgcn_cvt_pk_fp8_f32(q8_scaled(a << 16, s),
+                                                  q8_scaled(a & 0xffff0000u, s), (int)a, false);
+    c[h] = __builtin_amdgcn_cvt_pk_fp8_f32(q8_scaled(b << 16, s), q8_scaled(b & 0xffff0000u, s),
+                                           t, true);
+  }
+  v.x = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[0], false));
+  v.y = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[0], true));
+  v.z = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[1], false));
+  v.w = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[1], true));
+#else
+  (void)v, (void)s;
+#endif
 }
 
 // ----------------------------------------------------------------------
