@@ -196,6 +196,17 @@ struct LoaderMNMajor {
     return (u4comp(v[j], i >> 1) >> ((i & 1) * 16)) & 0xffffu;
   }
 
+  // Element i of vectors j and j+1 as one dword (j's in the low half): one
+  // byte permute of the dwords holding them.
+  __device__ __forceinline__ uint32_t pair(int j, int i) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    return __builtin_amdgcn_perm(u4comp(v[j + 1], i >> 1), u4comp(v[j], i >> 1),
+                                 (i & 1) ? 0x07060302u : 0x05040100u);
+#else
+    return elem(j, i) | (elem(j + 1, i) << 16);
+#endif
+  }
+
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
     const int kb = tid % KBN, mc = tid / KBN;
 #pragma unroll
@@ -204,19 +215,19 @@ struct LoaderMNMajor {
       uint16_t* dst = lds + row * kBK;
       if constexpr (L == 8) {
         uint4 o;
-        o.x = elem(0, i) | (elem(1, i) << 16);
-        o.y = elem(2, i) | (elem(3, i) << 16);
-        o.z = elem(4, i) | (elem(5, i) << 16);
-        o.w = elem(6, i) | (elem(7, i) << 16);
+        o.x = pair(0, i);
+        o.y = pair(2, i);
+        o.z = pair(4, i);
+        o.w = pair(6, i);
         *reinterpret_cast<uint4*>(dst + ((kb ^ swz(row)) << 3)) = o;
       } else if constexpr (L == 4) {
         uint2 o;
-        o.x = elem(0, i) | (elem(1, i) << 16);
-        o.y = elem(2, i) | (elem(3, i) << 16);
+        o.x = pair(0, i);
+        o.y = pair(2, i);
         *reinterpret_cast<uint2*>(dst + (((kb >> 1) ^ swz(row)) << 3) + (kb & 1) * 4) = o;
       } else {
         static_assert(L == 2, "panel rows must be 64, 128 or 256");
-        const uint32_t o = elem(0, i) | (elem(1, i) << 16);
+        const uint32_t o = pair(0, i);
         *reinterpret_cast<uint32_t*>(dst + (((kb >> 2) ^ swz(row)) << 3) + (kb & 3) * 2) = o;
       }
     }
