@@ -106,16 +106,24 @@ def test_nt_down_projection_full_size():
     w = workloads.nt_mlp()
     X = w["X"].to(dev())
     W = w["W"].to(dev())
+    # a small split-K product through the same kernel first, so that the
+    # runtime's per-kernel scratch memory is not counted below
+    d = workloads.random_operands(256, 512, 8192, "N", "T", seed=5)
+    run_store(d, "N", "T", 256, 512, 8192)
     torch.cuda.synchronize()
     free0 = torch.cuda.mem_get_info()[0]
+    torch.cuda.reset_peak_memory_stats()
+    base = torch.cuda.memory_allocated()
     Y = tgemm.matmul(X, W.t())              # a (1, 13824)-strided view: no copy
     torch.cuda.synchronize()
     free1 = torch.cuda.mem_get_info()[0]
     assert Y.shape == (384, 2, 5120)
-    # new device memory: the output (7.9 MB) and the split-K partial
-    # products the library allocates stream-ordered (at most 4 x 15.7 MB,
-    # which the memory pool may keep); a transposed copy of W would add
-    # 141.6 MB on top
+    # torch allocates the output alone (7.9 MB); a transposed copy of W
+    # would be 141.6 MB more
+    assert torch.cuda.max_memory_allocated() - base < 16 * 2 ** 20
+    # new device memory: the output and the split-K partial products the
+    # library allocates stream-ordered (4 x 15.7 MB, which the memory pool
+    # may round up)
     assert free0 - free1 < 128 * 2 ** 20
     rows = sample_rows(768, 48, seed=2)
     Xb = workloads.bf16_bits(w["X"]).reshape(-1)
