@@ -20,6 +20,8 @@
 // on the layout, the four layouts produce bitwise-identical results.
 #pragma once
 
+#include <type_traits>
+
 #include "bf16_cvt.h"
 #include "tgemm_internal.h"
 
@@ -108,6 +110,33 @@ __device__ __forceinline__ void q8_vec(uint4& v, float s) {
 // Operand loaders.  R = rows of the panel (M or N extent of the tile).
 // ----------------------------------------------------------------------
 
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+
+#if defined(__HIP_DEVICE_COMPILE__)
+// Buffer resource over `bytes` bytes from the wave-uniform address `origin`.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t panel_rsrc(const uint16_t* origin,
+                                                             uint32_t bytes) {
+  const uint64_t base = reinterpret_cast<uint64_t>(origin);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+  void* src = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+  // word 3 = 0x00020000: 32-bit data format, the raw-buffer setting
+  return __builtin_amdgcn_make_buffer_rsrc(src, (short)0,
+                                           (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
+}
+
+// 16-byte load at byte offset voff + soff (soff wave-uniform) of the buffer
+// `rs`.  Interior tiles load their panels this way: one resource per
+// panel and k-step (scalar registers), a per-thread byte offset fixed for
+// the whole kernel, and a uniform offset per vector, so a load is one
+// instruction with no address arithmetic or bounds test in the loop.
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t rs, uint32_t voff,
+                                            uint32_t soff) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)voff, (int)soff, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+#endif
+
 // Operand contiguous along K: stored row r (an m or n index) holds k.
 template <int R, int NTH = kThreads>
 struct LoaderKMajor {
@@ -136,10 +165,40 @@ struct LoaderKMajor {
     }
   }
 
+  // Interior tiles (the whole panel inside X, 16-byte aligned, ld % 8 ==
+  // 0, (R-1)*ld*2 < 2^32): vector i of thread t is row t/8 + i*NTH/8,
+  // chunk t%8 of the k-step, at a fixed per-thread byte offset plus i rows.
+  uint32_t voff, sstep;
+
+  __device__ __forceinline__ void init_interior(int64_t ld, int tid) {
+    voff = (uint32_t)(((int64_t)(tid >> 3) * ld + (tid & 7) * 8) * 2);
+    sstep = (uint32_t)(ld * (NTH / 8) * 2);
+  }
+
+  __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs =
+        panel_rsrc(X + (int64_t)r0 * ld + k0, (uint32_t)(((int64_t)(R - 1) * ld + kBK) * 2));
+#pragma unroll
+    for (int i = 0; i < L; ++i) v[i] = buf_load16(rs, voff, i * sstep);
+#else
+    (void)X, (void)ld, (void)r0, (void)k0;
+#endif
+  }
+
   // cast every loaded element to e4m3fn (Q8 epilogues); zero fill stays 0
   __device__ __forceinline__ void quantize(float sc) {
 #pragma unroll
     for (int i = 0; i < L; ++i) q8_vec(v[i], sc);
+  }
+
+  // The store as U units (one 16-byte LDS write each), so that they can be
+  // spread between matrix-core instructions.
+  static constexpr int U = L;
+  __device__ __forceinline__ void store_unit(uint16_t* lds, int tid, int i) const {
+    const int q = tid + NTH * i;
+    const int row = q >> 3, kc = q & 7;
+    *reinterpret_cast<uint4*>(lds + row * kBK + ((kc ^ swz(row)) << 3)) = v[i];
   }
 
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
@@ -187,6 +246,28 @@ struct LoaderMNMajor {
     }
   }
 
+  // Interior tiles (the whole panel inside X, 16-byte aligned, ld % 8 ==
+  // 0): vector j of thread t is k row kb*L + j, rows mc*8 .. +7, at a fixed
+  // per-thread byte offset plus j rows of X.
+  uint32_t voff, sstep;
+
+  __device__ __forceinline__ void init_interior(int64_t ld, int tid) {
+    const int kb = tid % KBN, mc = tid / KBN;
+    voff = (uint32_t)(((int64_t)kb * L * ld + mc * 8) * 2);
+    sstep = (uint32_t)(ld * 2);
+  }
+
+  __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const __amdgpu_buffer_rsrc_t rs =
+        panel_rsrc(X + (int64_t)k0 * ld + r0, (uint32_t)(((int64_t)(kBK - 1) * ld + R) * 2));
+#pragma unroll
+    for (int j = 0; j < L; ++j) v[j] = buf_load16(rs, voff, j * sstep);
+#else
+    (void)X, (void)ld, (void)r0, (void)k0;
+#endif
+  }
+
   __device__ __forceinline__ void quantize(float sc) {
 #pragma unroll
     for (int j = 0; j < L; ++j) q8_vec(v[j], sc);
@@ -205,6 +286,33 @@ struct LoaderMNMajor {
 #else
     return elem(j, i) | (elem(j + 1, i) << 16);
 #endif
+  }
+
+  // The store as U units (row i of the thread's 8 rows: the transposed
+  // element i of every vector, one LDS write), so that they can be spread
+  // between matrix-core instructions.
+  static constexpr int U = 8;
+  __device__ __forceinline__ void store_unit(uint16_t* lds, int tid, int i) const {
+    const int kb = tid % KBN, mc = tid / KBN;
+    const int row = mc * 8 + i;
+    uint16_t* dst = lds + row * kBK;
+    if constexpr (L == 8) {
+      uint4 o;
+      o.x = pair(0, i);
+      o.y = pair(2, i);
+      o.z = pair(4, i);
+      o.w = pair(6, i);
+      *reinterpret_cast<uint4*>(dst + ((kb ^ swz(row)) << 3)) = o;
+    } else if constexpr (L == 4) {
+      uint2 o;
+      o.x = pair(0, i);
+      o.y = pair(2, i);
+      *reinterpret_cast<uint2*>(dst + (((kb >> 1) ^ swz(row)) << 3) + (kb & 1) * 4) = o;
+    } else {
+      static_assert(L == 2, "panel rows must be 64, 128 or 256");
+      const uint32_t o = pair(0, i);
+      *reinterpret_cast<uint32_t*>(dst + (((kb >> 2) ^ swz(row)) << 3) + (kb & 3) * 2) = o;
+    }
   }
 
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
@@ -417,6 +525,37 @@ __device__ __forceinline__ void plain_substep(f32x16_t (&acc)[FM][FN], const bf1
     acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One k-substep of the register path: MFMA q, one fragment read of the
+// next substep (first FM+FN slots), and, when `st_on` is set, the LDS store
+// units of loaders `la` then `lb` (the next k-step's operand panels, into
+// `da` and `db`), spread evenly over the slots.
+template <int FM, int FN, bool SW, typename LdA, typename LdB>
+__device__ __forceinline__ void store2_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                               const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                               const uint16_t* rd_stage, int a_base, int b_base,
+                                               int xo, const LdA& la, const LdB& lb, uint16_t* da,
+                                               uint16_t* db, int tid, bool st_on) {
+  constexpr int SL = FM * FN, U = LdA::U + LdB::U;
+  const uint16_t* pa = rd_stage + a_base + xo;
+  const uint16_t* pb = rd_stage + b_base + xo;
+#pragma unroll
+  for (int q = 0; q < SL; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    if (st_on) {
+      // units u with floor(u * SL / U) == q
+#pragma unroll
+      for (int u = (q * U + SL - 1) / SL; u < U && (u * SL) / U == q; ++u) {
+        if (u < LdA::U) la.store_unit(da, tid, u);
+        else lb.store_unit(db, tid, u - LdA::U);
+      }
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -978,10 +1117,68 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       staged = true;
     }
   }
-  if (!staged) {
-    // General path: any layout, ragged edges, unaligned operands.  16-byte
-    // (or masked element) loads into registers, one k-step ahead, then
-    // (transposing if needed) stores into the other LDS stage.
+  // (both operands K-contiguous without the cast: interior tiles always take
+  // a direct-copy loop above, so this path is not compiled for them)
+  constexpr bool kRegInterior = !(A_KMAJOR && B_KMAJOR) || Q8;
+  if (kRegInterior && !staged && interior) {
+    // Register path, interior tiles: one buffer load per 16-byte vector and
+    // no bounds tests.  The loads of k-step kt+1 are issued right after the
+    // barrier of k-step kt-1 (when the register set is free again), and the
+    // set is written (transposed if needed) into the other LDS stage one
+    // unit per matrix-core instruction during the third substep of kt.
+    typename LoaderSel<A_KMAJOR, BM>::type la;
+    typename LoaderSel<B_KMAJOR, BN>::type lb;
+    const int nk = (kend - kbeg) / kBK;
+    la.init_interior(p.lda, tid);
+    lb.init_interior(p.ldb, tid);
+    float qa = 0.f, qb = 0.f;
+    if constexpr (Q8) {
+      qa = p.qscales[0];
+      qb = p.qscales[1];
+    }
+    la.load_interior(p.A, p.lda, m0, kbeg);
+    lb.load_interior(p.B, p.ldb, n0, kbeg);
+    if constexpr (Q8) {
+      la.quantize(qa);
+      lb.quantize(qb);
+    }
+    la.store(lds, tid);
+    lb.store(lds + SA, tid);
+    if (nk > 1) {
+      la.load_interior(p.A, p.lda, m0, kbeg + kBK);
+      lb.load_interior(p.B, p.ldb, n0, kbeg + kBK);
+    }
+    __syncthreads();
+    bf16x8_t fa[2][FM], fb[2][FN];
+    read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      const uint16_t* st = lds + cur * STAGE;
+      uint16_t* nx = lds + (cur ^ 1) * STAGE;
+      __builtin_amdgcn_sched_barrier(0);
+      plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[1]);
+      if constexpr (Q8) {
+        if (more) {
+          la.quantize(qa);
+          lb.quantize(qb);
+        }
+      }
+      plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
+      store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3], la,
+                                 lb, nx, nx + SA, tid, more);
+      __syncthreads();
+      if (kt + 2 < nk) {
+        la.load_interior(p.A, p.lda, m0, kbeg + (kt + 2) * kBK);
+        lb.load_interior(p.B, p.ldb, n0, kbeg + (kt + 2) * kBK);
+      }
+      // (in the last k-step this reads a stale stage that is never used)
+      plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
+    }
+  } else if (!staged) {
+    // General path: ragged edges, unaligned operands.  16-byte (or masked
+    // element) loads into registers, one k-step ahead, then (transposing if
+    // needed) stores into the other LDS stage.
     typename LoaderSel<A_KMAJOR, BM>::type la;
     typename LoaderSel<B_KMAJOR, BN>::type lb;
     const int nk = (kend - kbeg + kBK - 1) / kBK;
@@ -997,67 +1194,32 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     la.store(lds, tid);
     lb.store(lds + SA, tid);
     __syncthreads();
-    if constexpr (A_KMAJOR || B_KMAJOR) {
-      // Fragment reads of the next substep between the MFMAs (as in the
-      // two-stage loop); the next k-step's stores go between the third
-      // substep and the barrier.
-      bf16x8_t fa[2][FM], fb[2][FN];
-      read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
-      for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-          la.load(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, aligned, tid);
-          lb.load(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, aligned, tid);
-        }
-        const uint16_t* st = lds + cur * STAGE;
-        uint16_t* nx = lds + (cur ^ 1) * STAGE;
-        __builtin_amdgcn_sched_barrier(0);
-        plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[1]);
-        plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
-        plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3]);
-        if (more) {
-          if constexpr (Q8) {
-            la.quantize(qa);
-            lb.quantize(qb);
-          }
-          la.store(nx, tid);
-          lb.store(nx + SA, tid);
-        }
-        __syncthreads();
-        // (in the last k-step this reads a stale stage that is never used)
-        plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
+    bf16x8_t fa[2][FM], fb[2][FN];
+    read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      const bool more = kt + 1 < nk;
+      if (more) {
+        la.load(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, aligned, tid);
+        lb.load(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, aligned, tid);
       }
-    } else {
-      // Both operands MN-contiguous (TN): both stores transpose, and the
-      // loads want the whole k-step to land, so the stores come after all
-      // four substeps.  (Measured at 4096^3: 190-196 us here against
-      // 201-206 us for the loop above.)
-      for (int kt = 0; kt < nk; ++kt) {
-        const int cur = kt & 1;
-        const bool more = kt + 1 < nk;
-        if (more) {
-          la.load(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, aligned, tid);
-          lb.load(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, aligned, tid);
+      const uint16_t* st = lds + cur * STAGE;
+      uint16_t* nx = lds + (cur ^ 1) * STAGE;
+      __builtin_amdgcn_sched_barrier(0);
+      plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[1]);
+      plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
+      plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3]);
+      if (more) {
+        if constexpr (Q8) {
+          la.quantize(qa);
+          lb.quantize(qb);
         }
-        const uint16_t* st = lds + cur * STAGE;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          bf16x8_t af[FM], bfr[FN];
-          read_frags<FM, FN>(st, a_base, b_base, xo[s], af, bfr);
-          mfma_block<FM, FN, SW>(af, bfr, acc);
-        }
-        if (more) {
-          uint16_t* nx = lds + (cur ^ 1) * STAGE;
-          if constexpr (Q8) {
-            la.quantize(qa);
-            lb.quantize(qb);
-          }
-          la.store(nx, tid);
-          lb.store(nx + SA, tid);
-        }
-        __syncthreads();
+        la.store(nx, tid);
+        lb.store(nx + SA, tid);
       }
+      __syncthreads();
+      // (in the last k-step this reads a stale stage that is never used)
+      plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
     }
   }
 
