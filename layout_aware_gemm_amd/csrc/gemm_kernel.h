@@ -830,24 +830,41 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
     // (Q8: the sum times the output scale, one fp32 multiply)
     float os = 1.f;
     if constexpr (Q8) os = p.qscales[2];
+    // One output row at a time: its address is formed once, and the FN
+    // column blocks of the row are immediate offsets from it.  A wave whose
+    // whole block lies inside C stores without bounds tests.
+    const int col0 = n0 + wc0 + lc;
+    const bool full = m0 + wr0 + 32 * FM <= p.M && n0 + wc0 + 32 * FN <= p.N;
+    auto put = [&](int64_t off, float v) __attribute__((always_inline)) {
+      if constexpr (Q8) v = __fmul_rn(v, os);
+      if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16)
+        reinterpret_cast<uint16_t*>(p.C)[off] = to_bf16(v);
+      else
+        reinterpret_cast<float*>(p.C)[off] = v;
+    };
+    if (full) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int col = n0 + wc0 + j * 32 + lc;
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int row = m0 + wr0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (row < p.M && col < p.N) {
-            float v = acc[i][j][r];
-            if constexpr (Q8) v = __fmul_rn(v, os);
-            if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16)
-              reinterpret_cast<uint16_t*>(p.C)[(int64_t)row * p.ldc + col] = to_bf16(v);
-            else
-              reinterpret_cast<float*>(p.C)[(int64_t)row * p.ldc + col] = v;
-          }
+          const int64_t off = (int64_t)row * p.ldc + col0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j) put(off + j * 32, acc[i][j][r]);
         }
-      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wr0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+          if (row >= p.M) continue;
+          const int64_t off = (int64_t)row * p.ldc + col0;
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            if (col0 + j * 32 < p.N) put(off + j * 32, acc[i][j][r]);
+        }
+    }
   } else if constexpr (SW) {
     // Cross-entropy on transposed accumulators: block (i,j), register r of
     // lane l holds C[row i*32 + l%32][col j*32 + 8*(r/4) + 4*(l/32) + r%4].
