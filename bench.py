@@ -145,6 +145,30 @@ def cpu_oracle_secondary(budget_s=6.0):
     return out
 
 
+def layout_sweep(steps, warmup):
+    """The 4096^3 GEMM in the four layouts (same logical operands, each
+    stored in its layout's order): TFLOP/s per layout."""
+    import torch
+
+    import workloads
+    from layout_aware_gemm_amd import tgemm
+
+    dev = torch.device("cuda:0")
+    out = {}
+    ls = workloads.layout_sweep()
+    for ta, tb in [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]:
+        sa, lda = workloads.store_operand(ls["opA"], ta)
+        sb, ldb = workloads.store_operand(ls["opB"], tb)
+        A, B = sa.to(dev), sb.to(dev)
+        C = torch.empty(4096, 4096, dtype=torch.bfloat16, device=dev)
+        msl = time_stream(lambda i: tgemm.run(ta, tb, 4096, 4096, 4096, A, lda, B, ldb, C,
+                                              4096, tgemm.EPI_STORE_BF16), steps, warmup, 1)
+        out[f"sweep_{ta}{tb}_tflops"] = round(2.0 * 4096 ** 3 / (msl * 1e-3) / 1e12, 2)
+        out[f"sweep_{ta}{tb}_us"] = round(msl * 1e3, 2)
+        del A, B, C
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +177,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--only-nt", action="store_true",
                     help="time only the NT GEMM with rotated inputs (the profiled command)")
+    ap.add_argument("--only-sweep", action="store_true",
+                    help="time only the 4096^3 layout sweep (NN, NT, TN, TT) and print its "
+                         "figures (a profiling command; no headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE; "
@@ -183,6 +210,10 @@ def main():
         log(f"copied {COPY_CAL_BYTES} bytes 5 times")
         return 0
     K_, W_ = args.steps, args.warmup
+    if args.only_sweep:
+        log("timing the 4096^3 layout sweep ...")
+        print(json.dumps(layout_sweep(K_, W_)), flush=True)
+        return 0
 
     # ---- NT down-projection: the headline step --------------------------
     M, N, K = 768, 5120, 13824
@@ -248,17 +279,7 @@ def main():
         del Hs, Wv, g, dH, dW
 
         # ---- layout sweep 4096^3 ------------------------------------------
-        ls = workloads.layout_sweep()
-        for ta, tb in [("N", "N"), ("N", "T"), ("T", "N"), ("T", "T")]:
-            sa, lda = workloads.store_operand(ls["opA"], ta)
-            sb, ldb = workloads.store_operand(ls["opB"], tb)
-            A, B = sa.to(dev), sb.to(dev)
-            C = torch.empty(4096, 4096, dtype=torch.bfloat16, device=dev)
-            msl = time_stream(lambda i: tgemm.run(ta, tb, 4096, 4096, 4096, A, lda, B, ldb, C,
-                                                  4096, tgemm.EPI_STORE_BF16), K_, W_, 1)
-            secondary[f"sweep_{ta}{tb}_tflops"] = round(2.0 * 4096 ** 3 / (msl * 1e-3) / 1e12, 2)
-            del A, B, C
-        del ls
+        secondary.update(layout_sweep(K_, W_))
 
         # ---- matrix-vector and dot products (M = 1 or N = 1) ---------------
         wm = workloads.nt_mlp()
