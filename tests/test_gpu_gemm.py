@@ -241,3 +241,30 @@ def test_ragged_k64_layouts_bitwise(M, N, K, cfg):
             assert scaled_err(outs["NT"].cpu().numpy(), ref) <= 1e-4
     for k, v in outs.items():
         assert torch.equal(v, outs["TN"]), k
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("split", [2, 3])
+@pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (384, 200, 1536)])
+def test_split_k_all_layouts_bitwise(M, N, K, split, cfg):
+    """K cut into chunks in every layout: each chunk starts at a nonzero k
+    on the register path's interior loads (M- or N-contiguous operands) and
+    on the direct copies (NT).  Every layout gives the NT bits, NT matches
+    the oracle, and the bf16 output is the fp32 sum rounded once."""
+    outs, outs16 = {}, {}
+    prev = tgemm.set_split_k(split)
+    try:
+        for ta, tb in LAYOUTS:
+            d = workloads.random_operands(M, N, K, ta, tb, seed=7 * split + K)
+            outs[ta + tb] = run_store(d, ta, tb, M, N, K, out_dtype=torch.float32, cfg=cfg)
+            outs16[ta + tb] = run_store(d, ta, tb, M, N, K, cfg=cfg)
+            if ta + tb == "NT":
+                ref = oracle_gemm_from(d, ta, tb, M, N, K)
+    finally:
+        tgemm.set_split_k(prev)
+    assert scaled_err(outs["NT"].cpu().numpy(), ref) <= 1e-4
+    for k in outs:
+        assert torch.equal(outs[k], outs["NT"]), k
+        assert torch.equal(outs16[k], outs16["NT"]), k
+    assert np.array_equal(bits(outs16["NT"]),
+                          oracle.f64_to_bf16_bits(outs["NT"].cpu().numpy().astype(np.float64)))
