@@ -119,14 +119,15 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
         cw[q] = pack_bf16x2(cv8[2 * q], cv8[2 * q + 1]);
         sw[q] = pack_bf16x2(sv8[2 * q], sv8[2 * q + 1]);
       }
-      const uint4 cv = make_uint4(cw[0], cw[1], cw[2], cw[3]);
-      const uint4 sv = make_uint4(sw[0], sw[1], sw[2], sw[3]);
       uint16_t* co = cos_out + row * ldc;
       uint16_t* so = sin_out + row * ldc;
-      *reinterpret_cast<uint4*>(co + c0) = cv;
-      *reinterpret_cast<uint4*>(co + c0 + N) = cv;
-      *reinterpret_cast<uint4*>(so + c0) = sv;
-      *reinterpret_cast<uint4*>(so + c0 + N) = sv;
+      // streaming stores: the tables are written once and not read back here
+      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+      const u32x4 cq = {cw[0], cw[1], cw[2], cw[3]}, sq = {sw[0], sw[1], sw[2], sw[3]};
+      __builtin_nontemporal_store(cq, reinterpret_cast<u32x4*>(co + c0));
+      __builtin_nontemporal_store(cq, reinterpret_cast<u32x4*>(co + c0 + N));
+      __builtin_nontemporal_store(sq, reinterpret_cast<u32x4*>(so + c0));
+      __builtin_nontemporal_store(sq, reinterpret_cast<u32x4*>(so + c0 + N));
     }
   } else {
     for (int j = 0; j < RPT; ++j) {
