@@ -169,6 +169,44 @@ def layout_sweep(steps, warmup):
     return out
 
 
+def fused_ce(steps, warmup):
+    """The fused CE GEMM 4096x32000x4096 (inputs rotated between two
+    copies), loss only and loss + gradient.  Returns its figures and the
+    device tensors (H copies, W copies, gradient) for the backward GEMMs."""
+    import torch
+
+    import workloads
+    from layout_aware_gemm_amd import tgemm
+
+    dev = torch.device("cuda:0")
+    Mc, Nc, Kc = 4096, 32000, 4096
+    cv = workloads.ce_vocab()
+    Hs = [cv["H"].to(dev) for _ in range(2)]
+    Wv = [cv["W"].to(dev) for _ in range(2)]
+    lab = cv["labels"].to(dev)
+    del cv
+    loss = torch.empty(Mc, dtype=torch.float32, device=dev)
+
+    def ce_step(i, g=None):
+        tgemm.run("N", "T", Mc, Nc, Kc, Hs[i], Kc, Wv[i], Kc, None, Nc, tgemm.EPI_CE,
+                  labels=lab, out_loss=loss, out_grad=g)
+
+    log("timing fused CE 4096x32000x4096 ...")
+    ms_ce = time_stream(ce_step, steps, warmup, 2)
+    g = torch.empty(Mc, Nc, dtype=torch.bfloat16, device=dev)
+    ms_ceg = time_stream(lambda i: ce_step(i, g), steps, warmup, 2)
+    ce_fl = 2.0 * Mc * Nc * Kc
+    out = {
+        "ce_loss_rows_per_s": round(Mc / (ms_ce * 1e-3), 1),
+        "ce_loss_tflops": round(ce_fl / (ms_ce * 1e-3) / 1e12, 2),
+        "ce_loss_frac_of_peak": round(ce_fl / (ms_ce * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "ce_loss_ms": round(ms_ce, 4),
+        "ce_grad_rows_per_s": round(Mc / (ms_ceg * 1e-3), 1),
+        "ce_grad_ms": round(ms_ceg, 4),
+    }
+    return out, Hs, Wv, g
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -180,6 +218,9 @@ def main():
     ap.add_argument("--only-sweep", action="store_true",
                     help="time only the 4096^3 layout sweep (NN, NT, TN, TT) and print its "
                          "figures (a profiling command; no headline line)")
+    ap.add_argument("--only-ce", action="store_true",
+                    help="time only the fused CE GEMM 4096x32000x4096, loss only then loss + "
+                         "gradient, and print its figures (a profiling command; no headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE; "
@@ -210,6 +251,10 @@ def main():
         log(f"copied {COPY_CAL_BYTES} bytes 5 times")
         return 0
     K_, W_ = args.steps, args.warmup
+    if args.only_ce:
+        out, *_ = fused_ce(K_, W_)
+        print(json.dumps(out), flush=True)
+        return 0
     if args.only_sweep:
         log("timing the 4096^3 layout sweep ...")
         print(json.dumps(layout_sweep(K_, W_)), flush=True)
@@ -244,28 +289,9 @@ def main():
     if not args.only_nt:
         # ---- fused cross-entropy GEMM ------------------------------------
         Mc, Nc, Kc = 4096, 32000, 4096
-        cv = workloads.ce_vocab()
-        Hs = [cv["H"].to(dev) for _ in range(2)]
-        Wv = [cv["W"].to(dev) for _ in range(2)]
-        lab = cv["labels"].to(dev)
-        del cv
-        loss = torch.empty(Mc, dtype=torch.float32, device=dev)
-
-        def ce_step(i, g=None):
-            tgemm.run("N", "T", Mc, Nc, Kc, Hs[i], Kc, Wv[i], Kc, None, Nc, tgemm.EPI_CE,
-                      labels=lab, out_loss=loss, out_grad=g)
-
-        log("timing fused CE 4096x32000x4096 ...")
-        ms_ce = time_stream(ce_step, max(5, K_ // 5), max(2, W_ // 5), 2)
-        g = torch.empty(Mc, Nc, dtype=torch.bfloat16, device=dev)
-        ms_ceg = time_stream(lambda i: ce_step(i, g), max(5, K_ // 5), max(2, W_ // 5), 2)
+        ce_out, Hs, Wv, g = fused_ce(max(5, K_ // 5), max(2, W_ // 5))
+        secondary.update(ce_out)
         ce_fl = 2.0 * Mc * Nc * Kc
-        secondary["ce_loss_rows_per_s"] = round(Mc / (ms_ce * 1e-3), 1)
-        secondary["ce_loss_tflops"] = round(ce_fl / (ms_ce * 1e-3) / 1e12, 2)
-        secondary["ce_loss_frac_of_peak"] = round(ce_fl / (ms_ce * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)
-        secondary["ce_loss_ms"] = round(ms_ce, 4)
-        secondary["ce_grad_rows_per_s"] = round(Mc / (ms_ceg * 1e-3), 1)
-        secondary["ce_grad_ms"] = round(ms_ceg, 4)
         # the GEMMs that consume the gradient, operands read as stored:
         # dH = G . W (NN, K = 32000) and dW = G^T . H (TN, K = 4096)
         dH = torch.empty(Mc, Kc, dtype=torch.bfloat16, device=dev)
