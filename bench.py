@@ -207,6 +207,31 @@ def fused_ce(steps, warmup):
     return out, Hs, Wv, g
 
 
+def rope_tables(steps, warmup):
+    """The K=1 RoPE table (cos and sin, bf16 [P, 128]) for 4096 positions
+    and for 256 x 4096 positions: time, GB/s, fraction of HBM peak."""
+    import torch
+
+    import workloads
+    from layout_aware_gemm_amd import tgemm
+
+    dev = torch.device("cuda:0")
+    out = {}
+    for name, r in (("rope_4096", workloads.rope()), ("rope_256x4096", workloads.rope_batched(256))):
+        pos, inv = r["pos"].to(dev), r["inv_freq"].to(dev)
+        P = pos.numel()
+        cos = torch.empty(P, 128, dtype=torch.bfloat16, device=dev)
+        sin = torch.empty_like(cos)
+        msr = time_stream(lambda i: tgemm.run("N", "N", P, 64, 1, pos, 1, inv, 64, cos, 128,
+                                              tgemm.EPI_ROPE_COSSIN, out_grad=sin), steps, warmup, 1)
+        byts = 2 * P * 128 * 2 + P * 8 + 64 * 4
+        out[f"{name}_us"] = round(msr * 1e3, 2)
+        out[f"{name}_GBps"] = round(byts / (msr * 1e-3) / 1e9, 1)
+        out[f"{name}_frac_of_hbm"] = round(byts / (msr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+        del pos, inv, cos, sin
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -221,6 +246,9 @@ def main():
     ap.add_argument("--only-ce", action="store_true",
                     help="time only the fused CE GEMM 4096x32000x4096, loss only then loss + "
                          "gradient, and print its figures (a profiling command; no headline line)")
+    ap.add_argument("--only-rope", action="store_true",
+                    help="time only the K=1 RoPE table (4096 and 256 x 4096 positions) and print "
+                         "its figures (a profiling command; no headline line)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE; "
@@ -251,6 +279,9 @@ def main():
         log(f"copied {COPY_CAL_BYTES} bytes 5 times")
         return 0
     K_, W_ = args.steps, args.warmup
+    if args.only_rope:
+        print(json.dumps(rope_tables(K_, W_)), flush=True)
+        return 0
     if args.only_ce:
         out, *_ = fused_ce(K_, W_)
         print(json.dumps(out), flush=True)
@@ -365,18 +396,7 @@ def main():
         del Xf, Wf, Wft, Yf, sc
 
         # ---- K=1 RoPE table --------------------------------------------------
-        for name, r in (("rope_4096", workloads.rope()), ("rope_256x4096", workloads.rope_batched(256))):
-            pos, inv = r["pos"].to(dev), r["inv_freq"].to(dev)
-            P = pos.numel()
-            cos = torch.empty(P, 128, dtype=torch.bfloat16, device=dev)
-            sin = torch.empty_like(cos)
-            msr = time_stream(lambda i: tgemm.run("N", "N", P, 64, 1, pos, 1, inv, 64, cos, 128,
-                                                  tgemm.EPI_ROPE_COSSIN, out_grad=sin), K_, W_, 1)
-            byts = 2 * P * 128 * 2 + P * 8 + 64 * 4
-            secondary[f"{name}_us"] = round(msr * 1e3, 2)
-            secondary[f"{name}_GBps"] = round(byts / (msr * 1e-3) / 1e9, 1)
-            secondary[f"{name}_frac_of_hbm"] = round(byts / (msr * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
-            del pos, inv, cos, sin
+        secondary.update(rope_tables(K_, W_))
 
     traffic = measured_traffic()
     out = {
