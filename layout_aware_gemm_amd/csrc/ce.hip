@@ -22,46 +22,66 @@ constexpr float kLn2F = 0.6931471805599453f;
 __device__ __forceinline__ float exp_f(float x) { return exp2f(x * kLog2eF); }
 
 
-// (m, s) (+) (m', s') = (max, s e^{m-max} + s' e^{m'-max}); a pair with
-// s == 0 is the identity (-inf, 0) and is skipped, so -inf - -inf is never
-// evaluated.
-__device__ __forceinline__ void merge(float& m, float& s, float mt, float st) {
-  if (!(st > 0.f)) return;
-  if (s > 0.f) {
-    const float mx = fmaxf(m, mt);
-    s = s * exp_f(m - mx) + st * exp_f(mt - mx);
-    m = mx;
-  } else {
-    m = mt;
-    s = st;
-  }
-}
-
-// Workgroup = 16 rows x 16 lanes per row.  Lane q of a row folds the blocks
-// t = q, q+16, q+32, ... in ascending order; the 16 lane results are then
-// folded in ascending q.  A fixed order, so the result is deterministic.
-// Loads of one block index cover 16 consecutive rows (64 contiguous bytes).
-constexpr int kCombRows = 16, kCombParts = 16;
-
+// Workgroup = 64 rows x 16 parts; wave q takes part q, the blocks t = q,
+// q+16, q+32, ..., for 64 consecutive rows (one 256-byte load per block).
+// Two passes instead of a chain of pairwise merges: the row max over every
+// non-empty block, then the sum of s_t * exp(m_t - max), whose exponentials
+// are independent of each other.  Each part adds its blocks in ascending t
+// and the sixteen part sums are added in ascending part order: a fixed order,
+// so the result is deterministic.  A block with s == 0 holds no column and
+// is skipped; a block whose sum is NaN (a NaN logit, or exp(inf - inf))
+// makes the row's logsumexp NaN, and with it the loss and the gradient row.
+// This is the pairwise (m, s) (+) (m', s') = (M, s e^{m-M} + s' e^{m'-M})
+// merge unrolled: any order of merges gives the same max and, up to
+// rounding, the same sum.
+constexpr int kCombRows = 64, kCombParts = 16;
 __global__ void __launch_bounds__(kCombRows * kCombParts) ce_combine_kernel(
     const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ ylab,
     const int32_t* __restrict__ labels, int M, int N, int nblk, float* __restrict__ loss,
     float* __restrict__ lse_out) {
-  __shared__ float sm[kCombParts][kCombRows], ss[kCombParts][kCombRows];
+  __shared__ float red[kCombParts][kCombRows];
+  __shared__ int bad[kCombParts][kCombRows];
   const int r = threadIdx.x % kCombRows, q = threadIdx.x / kCombRows;
   const int row = blockIdx.x * kCombRows + r;
-  float m = -INFINITY, s = 0.f;
-  if (row < M) {
+  const bool live = row < M;
+  float m = -INFINITY;
+  int nan_seen = 0;
+  if (live) {
 #pragma unroll 4
-    for (int t = q; t < nblk; t += kCombParts)
-      merge(m, s, pm[(int64_t)t * M + row], ps[(int64_t)t * M + row]);
+    for (int t = q; t < nblk; t += kCombParts) {
+      const int64_t i = (int64_t)t * M + row;
+      const float st = ps[i];
+      if (st > 0.f) m = fmaxf(m, pm[i]);
+      else if (st != st) nan_seen = 1;
+    }
   }
-  sm[q][r] = m;
-  ss[q][r] = s;
+  red[q][r] = m;
+  bad[q][r] = nan_seen;
   __syncthreads();
-  if (q != 0 || row >= M) return;
-  for (int j = 1; j < kCombParts; ++j) merge(m, s, sm[j][r], ss[j][r]);
-  const float lse = m + log2f(s) * kLn2F;
+  float mx = red[0][r];
+  int any_nan = bad[0][r];
+#pragma unroll
+  for (int j = 1; j < kCombParts; ++j) {
+    mx = fmaxf(mx, red[j][r]);
+    any_nan |= bad[j][r];
+  }
+  __syncthreads();
+  float sum = 0.f;
+  if (live) {
+#pragma unroll 4
+    for (int t = q; t < nblk; t += kCombParts) {
+      const int64_t i = (int64_t)t * M + row;
+      const float st = ps[i];
+      if (st > 0.f) sum += st * exp_f(pm[i] - mx);
+    }
+  }
+  red[q][r] = sum;
+  __syncthreads();
+  if (q != 0 || !live) return;
+  float s = red[0][r];
+#pragma unroll
+  for (int j = 1; j < kCombParts; ++j) s += red[j][r];
+  const float lse = any_nan ? __int_as_float(0x7fc00000) : mx + log2f(s) * kLn2F;
   const int lab = labels[row];
   loss[row] = (lab >= 0 && lab < N) ? lse - ylab[row] : __int_as_float(0x7fc00000);
   lse_out[row] = lse;

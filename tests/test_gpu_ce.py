@@ -106,6 +106,31 @@ def test_out_of_range_labels_give_nan():
     assert scaled_err(bf16_to_f64(g), ref_grad) <= GEMM_BF16_TOL
 
 
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_nan_logit_propagates_to_its_row(cfg):
+    """A NaN in row i of A makes every logit of row i NaN: that row's loss
+    and gradient row are NaN (the oracle's fp64 result is NaN too), and the
+    other rows still match the oracle."""
+    M, N, K = 70, 600, 64
+    d = workloads.random_operands(M, N, K, "N", "T", seed=12)
+    A = d["A"].clone()
+    A[5, 3] = float("nan")
+    labels = torch.randint(0, N, (M,), generator=torch.Generator().manual_seed(8),
+                           dtype=torch.int32)
+    loss, g = run_ce(A.to(dev()), K, d["B"].to(dev()), K, labels.to(dev()), M, N, K, grad=True,
+                     cfg=cfg)
+    l = loss.cpu().numpy()
+    ref_loss, ref_grad, _ = oracle_ce({"A": A, "lda": K, "B": d["B"], "ldb": K}, "N", "T", M, N,
+                                      K, labels)
+    assert np.isnan(ref_loss[5]) and np.isnan(l[5])
+    gg = bf16_to_f64(g)
+    assert np.all(np.isnan(gg[5]))
+    ok = np.arange(M) != 5
+    assert np.all(np.isfinite(l[ok]))
+    assert rel_err(l[ok], ref_loss[ok]) <= LOSS_REL_TOL
+    assert scaled_err(gg[ok], ref_grad[ok]) <= GEMM_BF16_TOL
+
+
 def test_ce_deterministic_and_grad_mode_same_loss():
     M, N, K = 512, 3000, 256
     d = workloads.random_operands(M, N, K, "N", "T", seed=9)
