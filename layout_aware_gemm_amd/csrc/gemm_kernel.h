@@ -3,11 +3,14 @@
 //
 // Structure of one workgroup (256 threads = 4 wave64s in a 2x2 grid):
 //   * it owns a BM x BN output tile and walks K in steps of 64;
-//   * each k-step, every thread fetches its share of the A and B panels
-//     with 16-byte global loads along the operand's contiguous axis into
-//     registers (the next step's loads are in flight while the current step
-//     computes), then writes them to the other half of a double-buffered
-//     LDS tile;
+//   * operand panels reach LDS one of two ways.  Interior tiles with both
+//     operands K-contiguous (NT) copy them straight from global memory into
+//     LDS (buffer loads with an LDS destination; three B panels and two A
+//     panels for 256x256 tiles, a ring of k32 stages for 128x128).  Every
+//     other case -- an operand contiguous along M or N, the fp8 cast, edge
+//     tiles -- loads 16-byte vectors along the operand's contiguous axis
+//     into registers a k-step ahead and then writes them to the other half
+//     of a double-buffered LDS tile;
 //   * LDS always holds both panels K-contiguous ([rows][64] bf16, 128 B per
 //     row) with the 16-byte chunks XOR-swizzled, so the matrix-core operand
 //     reads below are identical for every layout.  An operand that is
@@ -560,40 +563,6 @@ __device__ __forceinline__ void store2_substep(f32x16_t (&acc)[FM][FN], const bf
   }
 }
 
-// One k-substep of the fast path, written as FM*FN issue slots.  Slot q
-// issues MFMA q of the current fragments and then its side work: the
-// fragment reads of the next substep (one per slot, first FM+FN slots) and,
-// when `dma` is set, NCS global->LDS copies (blocks dma0 .. dma0+NCS-1 of
-// the stage, A's blocks first), one every FM*FN/NCS slots.  Scheduling
-// fences between slots keep this order, so the copies and LDS reads are
-// spread between matrix-core instructions instead of bunching up.
-template <int FM, int FN, int NCS, int NA, int NB, bool SW = false>
-__device__ __forceinline__ void substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
-                                        const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
-                                        const uint16_t* rd_stage, int a_base, int b_base, int xo,
-                                        bool dma, int dma0, const DmaPanel<NA * 32>& da,
-                                        const DmaPanel<NB * 32>& db, const uint16_t* oa,
-                                        const uint16_t* ob, uint16_t* dst, int wave_u) {
-  constexpr int SA = NA * 32 * kBK;
-  constexpr int STEP = FM * FN / NCS;
-  static_assert(NCS > 0 && STEP * NCS == FM * FN, "copies must divide the slots evenly");
-  const uint16_t* pa = rd_stage + a_base + xo;
-  const uint16_t* pb = rd_stage + b_base + xo;
-#pragma unroll
-  for (int q = 0; q < FM * FN; ++q) {
-    const int i = q / FN, j = q % FN;
-    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
-    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
-    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
-    if (dma && q % STEP == 0) {
-      const int n = dma0 + q / STEP;
-      if (n < NA) da.issue_one(oa, dst, wave_u, n);
-      else if (n < NA + NB) db.issue_one(ob, dst + SA, wave_u, n - NA);
-    }
-    __builtin_amdgcn_sched_barrier(0);
-  }
-}
-
 // ----------------------------------------------------------------------
 // Ring pipeline for interior tiles of K-contiguous operands.
 //
@@ -999,30 +968,52 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
 }
 
 // ----------------------------------------------------------------------
-// Two-stage pipeline (k-step 64) for interior tiles of K-contiguous
-// operands, four 16-k substeps per k-step and one barrier per k-step.
-// Used for 256x256 tiles, whose LDS traffic per k-step (not copy latency)
-// bounds them, so a deeper ring buys nothing there.
-//
-// A stage is free as soon as the barrier of the k-step that read it has
-// passed, so the copies of k-step kt+2 start right after the barrier of
-// k-step kt, in its last substep: half of them there and the other half
-// in the first substep of k-step kt+1, one copy every other MFMA.  Issued
-// at once, 64 copies per compute unit queue up in the texture path and
-// stall the issuing waves; issued later, they land after the barrier that
-// needs them.  (Measured on the 768x5120x13824 NT GEMM: 8-9% faster than
-// issuing all copies of k-step kt+1 in the first substep of k-step kt.)
-// k-steps [k0/64, k0/64 + nk).
+// Three-buffer pipeline for 256x256 interior tiles of K-contiguous operands
+// (k-step 64, four substeps, one barrier per k-step).  LDS holds two A
+// panels and three B panels of 32 KB each, the whole 160 KB.  B -- the
+// weight, the operand that streams from HBM -- is copied a k-step earlier
+// than A: the copies of B for k-step kt+2 go out in the first substep of
+// kt, into the buffer k-step kt-1 used, and have about six substeps to
+// land; the copies of A for k-step kt+2 go out after the barrier of kt, in
+// its last substep, into the buffer kt used.  Each substep that copies
+// issues one copy every other MFMA.  At the barrier of k-step kt only the
+// copies of B for kt+2 may still be in flight, so one wait covers both
+// operands of kt+1.
 // ----------------------------------------------------------------------
+
+// One substep: MFMA q, one fragment read of the next substep (first FM+FN
+// slots, from pa / pb), and, when `cp` is set, this wave's copies of one
+// panel (d, origin o, into dst), spread evenly over the slots.
+template <int FM, int FN, int R, bool SW>
+__device__ __forceinline__ void copy_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                             const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                             const uint16_t* pa, const uint16_t* pb, bool cp,
+                                             const DmaPanel<R>& d, const uint16_t* o,
+                                             uint16_t* dst, int wave_u) {
+  constexpr int NCP = DmaPanel<R>::PER_WAVE;
+  constexpr int STEP = FM * FN / NCP;
+  static_assert(STEP * NCP == FM * FN, "copies must divide the slots evenly");
+#pragma unroll
+  for (int q = 0; q < FM * FN; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    if (cp && q % STEP == 0) d.issue_one(o, dst, wave_u, q / STEP);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// k-steps [k0/64, k0/64 + nk).  a_base / b_local: element offsets of the
+// lane's first A / B fragment row inside a panel buffer.
 template <int BM, int BN, int FM, int FN, bool SW = false>
-__device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
+__device__ __forceinline__ void dma3_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
                                               uint16_t* lds, int wave, int lane, int a_base,
-                                              int b_base, const int* xo,
+                                              int b_local, const int* xo,
                                               f32x16_t (&acc)[FM][FN]) {
-  constexpr int SA = BM * kBK, STAGE = (BM + BN) * kBK;
-  constexpr int NA = BM / 32, NB = BN / 32;  // 1 KB copies per wave and k-step
-  constexpr int H = (NA + NB) / 2;           // copies per half
-  static_assert((NA + NB) % 2 == 0, "the copies of a k-step split in two halves");
+  constexpr int SA = BM * kBK, SB = BN * kBK;
+  constexpr int NA = DmaPanel<BM>::PER_WAVE, NB = DmaPanel<BN>::PER_WAVE;
+  static_assert(NA == NB, "one wait count for both operands");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   DmaPanel<BM> da;
   DmaPanel<BN> db;
@@ -1030,44 +1021,49 @@ __device__ __forceinline__ void dma2_mainloop(const GemmParams& p, int m0, int n
   db.init(p.ldb, wave, lane);
   const uint16_t* oa = p.A + (int64_t)m0 * p.lda + k0;
   const uint16_t* ob = p.B + (int64_t)n0 * p.ldb + k0;
-  // Prologue: k-step 0 whole, then the first half of k-step 1.  (k-steps
-  // past the end re-read k-step 0 into a stage that is never multiplied,
-  // which keeps the copy counts, and so the waits, uniform.)
-  da.issue(oa, lds, wave_u);
-  db.issue(ob, lds + SA, wave_u);
-  {
-    const int k1 = nk > 1 ? kBK : 0;
-#pragma unroll
-    for (int n = 0; n < H; ++n) {
-      if (n < NA) da.issue_one(oa + k1, lds + STAGE, wave_u, n);
-      else db.issue_one(ob + k1, lds + STAGE + SA, wave_u, n - NA);
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(H, 0));  // k-step 0 landed (own copies)
-  __syncthreads();
+  uint16_t* const abuf = lds;            // two A panels
+  uint16_t* const bbuf = lds + 2 * SA;   // three B panels
+  // k-steps past the end re-read k-step 0 into a buffer that is never
+  // multiplied, which keeps the copy counts, and so the waits, uniform
+  auto kof = [nk](int t) { return (t < nk ? t : 0) * kBK; };
+  // Prologue: A(0), B(0), B(1), A(1), in this order.
+  da.issue(oa + kof(0), abuf, wave_u);
+  db.issue(ob + kof(0), bbuf, wave_u);
+  db.issue(ob + kof(1), bbuf + SB, wave_u);
+  da.issue(oa + kof(1), abuf + SA, wave_u);
+  // A(0), B(0) landed (own copies; other waves: the barrier).  A raw
+  // barrier: the compiler's __syncthreads would also wait for B(1), A(1).
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(NA + NB, 0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
   bf16x8_t fa[2][FM], fb[2][FN];
-  read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+  read_frags<FM, FN>(abuf, a_base, b_local + 2 * SA, xo[0], fa[0], fb[0]);
+  int b3 = 0;  // kt % 3
   for (int kt = 0; kt < nk; ++kt) {
-    uint16_t* cur = lds + (kt & 1) * STAGE;
-    uint16_t* nxt = lds + ((kt & 1) ^ 1) * STAGE;
-    const int k1 = (kt + 1 < nk) ? (kt + 1) * kBK : 0;
-    const int k2 = (kt + 2 < nk) ? (kt + 2) * kBK : 0;
+    const int b3n = b3 == 2 ? 0 : b3 + 1;  // (kt + 1) % 3
+    const int b3p = b3 == 0 ? 2 : b3 - 1;  // (kt + 2) % 3, the buffer k-step kt-1 used
+    const uint16_t* ac = abuf + (kt & 1) * SA + a_base;
+    const uint16_t* bc = bbuf + b3 * SB + b_local;
+    const uint16_t* an = abuf + ((kt + 1) & 1) * SA + a_base;
+    const uint16_t* bn = bbuf + b3n * SB + b_local;
     __builtin_amdgcn_sched_barrier(0);
-    // second half of k-step kt+1 into the other stage
-    substep<FM, FN, H, NA, NB, SW>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[1],
-                                   true, H, da, db, oa + k1, ob + k1, nxt, wave_u);
-    substep<FM, FN, H, NA, NB, SW>(acc, fa[1], fb[1], fa[0], fb[0], cur, a_base, b_base, xo[2],
-                                   false, 0, da, db, oa, ob, nxt, wave_u);
-    substep<FM, FN, H, NA, NB, SW>(acc, fa[0], fb[0], fa[1], fb[1], cur, a_base, b_base, xo[3],
-                                   false, 0, da, db, oa, ob, nxt, wave_u);
-    // Every fragment of stage kt is in registers.  k-step kt+1 must have
-    // landed (own wave: vmcnt; other waves: the barrier) before it is read;
-    // after the barrier no wave reads stage kt any more.
-    wait_dma();
-    __syncthreads();
-    // first half of k-step kt+2 into the stage just released
-    substep<FM, FN, H, NA, NB, SW>(acc, fa[1], fb[1], fa[0], fb[0], nxt, a_base, b_base, xo[0],
-                                   true, 0, da, db, oa + k2, ob + k2, cur, wave_u);
+    copy_substep<FM, FN, BN, SW>(acc, fa[0], fb[0], fa[1], fb[1], ac + xo[1], bc + xo[1], true, db,
+                                 ob + kof(kt + 2), bbuf + b3p * SB, wave_u);
+    copy_substep<FM, FN, BN, SW>(acc, fa[1], fb[1], fa[0], fb[0], ac + xo[2], bc + xo[2], false,
+                                 db, ob, bbuf, wave_u);
+    copy_substep<FM, FN, BN, SW>(acc, fa[0], fb[0], fa[1], fb[1], ac + xo[3], bc + xo[3], false,
+                                 db, ob, bbuf, wave_u);
+    // A(kt+1) and B(kt+1) landed (own copies: all but the NB just issued;
+    // other waves: the barrier), and every LDS read of this wave is done
+    // (lgkmcnt 0), so after the barrier no wave reads A(kt) any more.  A
+    // raw barrier: the compiler's __syncthreads would also wait for the
+    // copies of B(kt+2).
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(NB, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    copy_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], an + xo[0], bn + xo[0], true, da,
+                                 oa + kof(kt + 2), abuf + (kt & 1) * SA, wave_u);
+    b3 = b3n;
   }
   // the trailing re-reads must land before the LDS is reused or released
   wait_dma();
@@ -1125,8 +1121,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   // (the direct copies move raw bf16, so Q8 operands take the register path)
   if constexpr (A_KMAJOR && B_KMAJOR && !Q8) {
     if (interior && BM == 256) {
-      dma2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
-                                        a_base, b_base, xo, acc);
+      static_assert(BM != 256 || 2 * SA + 3 * SB <= LDS_ELEMS, "three B panels must fit");
+      dma3_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
+                                        a_base, b_base - SA, xo, acc);
       staged = true;
     } else if (interior) {
       ring_mainloop<BM, BN, FM, FN, A_KMAJOR, B_KMAJOR, SW>(p, m0, n0, kbeg, (kend - kbeg) / kRK,
