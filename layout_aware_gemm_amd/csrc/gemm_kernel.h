@@ -358,17 +358,22 @@ struct LoaderSel<false, R, NTH> {
 // Workgroup -> tile mapping.  Workgroups are dealt round-robin to the 8
 // XCDs (workgroup b runs on XCD b % 8), each with its own L2.  The first
 // 8*floor(W/8) workgroups are renumbered so XCD x gets a contiguous range
-// of logical workgroups; consecutive logical workgroups are the `split`
-// K chunks of one tile, then the next tile.  Tiles are ordered in groups
-// of `groupM` tile rows (column-major inside a group), so the tiles one
-// XCD runs at the same time share A rows and B columns in its L2.
+// of logical workgroups.  With K split into `split` chunks the logical
+// order is chunk-major -- all tiles of chunk 0, then chunk 1 -- so an XCD
+// holds one K chunk of a run of tiles and reads only that chunk of the
+// operands shared along M or N (measured on the 768x5120x13824 NT GEMM:
+// a quarter of the X traffic, 3% faster at the sustained clock).  Tiles
+// are ordered in groups of `groupM` tile rows (column-major inside a
+// group), so the tiles one XCD runs at the same time share A rows and B
+// columns in its L2.
 // ----------------------------------------------------------------------
 __device__ __forceinline__ void xcd_remap(int bid, int W, int split, int& tile, int& ks) {
   const int per = W >> 3;
   int l = bid;
   if (bid < per * 8) l = (bid & 7) * per + (bid >> 3);
-  tile = l / split;
-  ks = l - tile * split;
+  const int ntiles = W / split;
+  ks = l / ntiles;
+  tile = l - ks * ntiles;
 }
 
 __device__ __forceinline__ void tile_coords(int t, int tilesM, int tilesN, int groupM, int& tm,
