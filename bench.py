@@ -57,10 +57,14 @@ def measured_traffic():
     return float(m_val.group(1))
 
 
-def time_stream(fn, steps, warmup, rotate):
+def time_stream(fn, steps, warmup, rotate, probe=None):
     """Average ms per call, HIP events on the current stream (the one tgemm
-    launches on), bracketed by synchronisation."""
+    launches on), bracketed by synchronisation.  With ``probe`` (an int64[3]
+    device tensor) the shader-clock probe is enqueued right after the end
+    event, outside the timed region, and reads the clock the region ended at."""
     import torch
+
+    from layout_aware_gemm_amd import tgemm
 
     for i in range(warmup):
         fn(i % rotate)
@@ -71,6 +75,8 @@ def time_stream(fn, steps, warmup, rotate):
     for i in range(steps):
         fn(i % rotate)
     end.record()
+    if probe is not None:
+        tgemm.clock_probe(out=probe)
     torch.cuda.synchronize()
     return start.elapsed_time(end) / steps
 
@@ -192,7 +198,9 @@ def fused_ce(steps, warmup):
                   labels=lab, out_loss=loss, out_grad=g)
 
     log("timing fused CE 4096x32000x4096 ...")
-    ms_ce = time_stream(ce_step, steps, warmup, 2)
+    probe = torch.zeros(3, dtype=torch.int64, device=dev)
+    ms_ce = time_stream(ce_step, steps, warmup, 2, probe=probe)
+    sclk_ce = tgemm.clock_ghz(probe)
     g = torch.empty(Mc, Nc, dtype=torch.bfloat16, device=dev)
     ms_ceg = time_stream(lambda i: ce_step(i, g), steps, warmup, 2)
     ce_fl = 2.0 * Mc * Nc * Kc
@@ -201,6 +209,7 @@ def fused_ce(steps, warmup):
         "ce_loss_tflops": round(ce_fl / (ms_ce * 1e-3) / 1e12, 2),
         "ce_loss_frac_of_peak": round(ce_fl / (ms_ce * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "ce_loss_ms": round(ms_ce, 4),
+        "ce_loss_sclk_ghz_end_of_timed": round(sclk_ce, 3),
         "ce_grad_rows_per_s": round(Mc / (ms_ceg * 1e-3), 1),
         "ce_grad_ms": round(ms_ceg, 4),
     }
@@ -306,9 +315,14 @@ def main():
         tgemm.run("N", "T", M, N, K, Xv[i], K, Ws[i], K, Ys[i], N, tgemm.EPI_STORE_BF16)
 
     log("timing NT 768x5120x13824 ...")
-    ms = time_stream(nt_step, K_, W_, copies)
+    # shader clock of the idle device, then at the end of the timed region
+    sclk_idle = tgemm.clock_ghz(tgemm.clock_probe())
+    probe = torch.zeros(3, dtype=torch.int64, device=dev)
+    ms = time_stream(nt_step, K_, W_, copies, probe=probe)
+    sclk_end = tgemm.clock_ghz(probe)
     tflops = flops / (ms * 1e-3) / 1e12
-    log(f"NT: {ms * 1e3:.1f} us/step ({tflops:.1f} TFLOP/s)")
+    log(f"NT: {ms * 1e3:.1f} us/step ({tflops:.1f} TFLOP/s); shader clock {sclk_idle:.2f} GHz "
+        f"idle, {sclk_end:.2f} GHz at the end of the timed steps")
     secondary = {}
     if not args.only_nt:
         # the same operands every step (they stay in the last-level cache)
@@ -418,6 +432,13 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic},
+        # the clock-adjusted view: the same rate against the peak at the shader
+        # clock read right after the timed steps (the chip lowers its clock
+        # under sustained matrix-core load)
+        "clock": {"sclk_ghz_idle": round(sclk_idle, 3),
+                  "sclk_ghz_end_of_timed": round(sclk_end, 3),
+                  "peak_at_that_sclk": round(PEAK_BF16_TFLOPS * sclk_end / 2.4, 1),
+                  "frac_at_that_sclk": round(tflops / (PEAK_BF16_TFLOPS * sclk_end / 2.4), 4)},
         "secondary": secondary,
     }
     if not args.no_cpu_baseline:

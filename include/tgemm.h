@@ -205,6 +205,21 @@ TGEMM_API int tgemm_set_tile_config(int config);
  */
 TGEMM_API int tgemm_set_split_k(int split);
 
+/*
+ * Measurement aid, beside the GEMM path: the shader clock the device runs
+ * at.  Enqueues on `stream` one wave that polls the device's constant-rate
+ * counter until it has advanced by `ticks` (1 <= ticks <= 10^7; at the
+ * usual 100 MHz rate, 2000 ticks = 20 us), then writes three uint64 values
+ * to out_ticks (device memory, 8-byte aligned, owned by the caller): the
+ * shader-clock cycles that elapsed, the constant-rate ticks that elapsed,
+ * and the constant rate in Hz.  The shader clock over the wait is
+ * out[0] * out[2] / out[1].  Enqueued right after a timed region it reads
+ * the clock that region ended at.  Asynchronous like tgemm_run.  Returns
+ * TGEMM_OK, TGEMM_ERR_INVALID_ARG (ticks out of range, NULL or misaligned
+ * out_ticks; checked before any device call) or TGEMM_ERR_HIP.
+ */
+TGEMM_API int tgemm_clock_probe(int64_t ticks, uint64_t* out_ticks, void* stream);
+
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 TGEMM_API int tgemm_version(void);
 

@@ -30,7 +30,8 @@ EPI_OUTER_F32 = 3
 EPI_ROPE_COSSIN = 4
 
 EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
-           "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k", "tgemm_version")
+           "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k",
+           "tgemm_clock_probe", "tgemm_version")
 
 
 class TgemmError(RuntimeError):
@@ -71,6 +72,8 @@ def lib():
         L.tgemm_set_tile_config.restype = ctypes.c_int
         L.tgemm_set_split_k.argtypes = [ctypes.c_int]
         L.tgemm_set_split_k.restype = ctypes.c_int
+        L.tgemm_clock_probe.argtypes = [i64, vp, vp]
+        L.tgemm_clock_probe.restype = ctypes.c_int
         L.tgemm_version.argtypes = []
         L.tgemm_version.restype = ctypes.c_int
         _lib = L
@@ -159,6 +162,27 @@ def set_split_k(split):
     if r < 0:
         raise TgemmError(r, "tgemm_set_split_k")
     return r
+
+
+def clock_probe(ticks=2000, out=None, stream=None):
+    """Enqueue the shader-clock probe (``tgemm_clock_probe``) and return the
+    int64[3] device tensor it fills: shader cycles, constant-rate ticks and
+    the constant rate in Hz.  ``clock_ghz`` reads the clock from it once the
+    stream has reached it."""
+    if out is None:
+        out = torch.zeros(3, dtype=torch.int64, device="cuda")
+    if out.dtype != torch.int64 or out.numel() < 3 or not out.is_cuda:
+        raise ValueError("clock_probe: out must be a CUDA int64 tensor of 3 elements")
+    r = lib().tgemm_clock_probe(int(ticks), _ptr(out), _stream(stream, out.device))
+    if r != 0:
+        raise TgemmError(r, "tgemm_clock_probe")
+    return out
+
+
+def clock_ghz(probe_out):
+    """Shader clock in GHz from a filled ``clock_probe`` tensor (synchronises)."""
+    cyc, ticks, rate = (int(v) for v in probe_out.cpu().tolist()[:3])
+    return cyc * rate / ticks / 1e9 if ticks > 0 else float("nan")
 
 
 def layout_of(x):

@@ -140,3 +140,12 @@ def test_run_fp8_rejects_before_touching_the_gpu():
     st = tgemm.run_fp8("N", "T", 64, 32, 48, 16, 48, 16, 48, 16, 32, tgemm.EPI_CE, 16, stream=0,
                        check=False)
     assert st == tgemm.TGEMM_ERR_INVALID_ARG
+
+
+def test_clock_probe_rejects_before_touching_the_gpu():
+    # ticks out of range, NULL or misaligned output: the status, no HIP call
+    L = tgemm.lib()
+    assert L.tgemm_clock_probe(2000, None, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_clock_probe(0, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_clock_probe(10 ** 7 + 1, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_clock_probe(2000, 20, None) == tgemm.TGEMM_ERR_INVALID_ARG
