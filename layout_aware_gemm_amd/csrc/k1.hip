@@ -63,11 +63,15 @@ __device__ __forceinline__ void sincos_t(float t, float& sn, float& cs) {
   }
 }
 
-// Rows per thread of the RoPE kernel.  A thread takes RPT rows that are
-// `slots` rows apart (so the lanes of one store instruction still cover
-// consecutive rows), loads all RPT positions first and then computes and
-// stores each row: the position loads overlap each other and the trig of
-// the earlier rows.
+// Rows per thread of the RoPE kernel.  A thread loads all RPT positions
+// first and then computes and stores each row: the position loads overlap
+// each other and the trig of the earlier rows.  When the column groups of
+// a row divide the 256 threads of a workgroup (spb = 256 / groups row
+// slots per workgroup), workgroup b writes the RPT*spb consecutive rows
+// from b*RPT*spb on, thread slot s its rows s, s + spb, ...: each
+// workgroup fills one contiguous block of both tables, and the lanes of one
+// store instruction still cover consecutive rows.  Otherwise (spb = 0) a
+// thread takes RPT rows that are `slots` rows apart.
 constexpr int kRopeRows = 2;
 
 // One thread per (row slot, group of 8 columns).
@@ -75,10 +79,11 @@ template <int RPT>
 __global__ void __launch_bounds__(256) k1_rope_kernel(
     const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf, int64_t sinv,
     int M, int N, uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out, int64_t ldc,
-    int vec_ok) {
+    int vec_ok, uint32_t spb) {
   // (the grid has fewer than 2^32 threads, so 32-bit index arithmetic)
   const uint32_t groups = (uint32_t)(N + 7) >> 3;
-  const uint32_t slots = ((uint32_t)M + RPT - 1) / RPT;
+  const uint32_t slots = spb ? ((uint32_t)M + spb * RPT - 1) / (spb * RPT) * spb
+                            : ((uint32_t)M + RPT - 1) / RPT;
   const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t rs = gid / groups;
   if (rs >= slots) return;
@@ -86,7 +91,8 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
   float pf[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) {
-    const int64_t row = (int64_t)rs + (int64_t)j * slots;
+    const int64_t row = spb ? (int64_t)(rs / spb) * spb * RPT + (int64_t)j * spb + rs % spb
+                             : (int64_t)rs + (int64_t)j * slots;
     const int64_t pv = row < M ? pos[row * spos] : 0;
     // int64 -> fp32, rounded to nearest even (exact below 2^24); one
     // instruction when the position fits in 32 bits
@@ -98,7 +104,8 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
     const float fr[8] = {f0.x, f0.y, f0.z, f0.w, f1.x, f1.y, f1.z, f1.w};
 #pragma unroll
     for (int j = 0; j < RPT; ++j) {
-      const int64_t row = (int64_t)rs + (int64_t)j * slots;
+      const int64_t row = spb ? (int64_t)(rs / spb) * spb * RPT + (int64_t)j * spb + rs % spb
+                             : (int64_t)rs + (int64_t)j * slots;
       if (row >= M) break;
       float t[8], sv8[8], cv8[8], m = 0.f;
 #pragma unroll
@@ -131,7 +138,8 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
     }
   } else {
     for (int j = 0; j < RPT; ++j) {
-      const int64_t row = (int64_t)rs + (int64_t)j * slots;
+      const int64_t row = spb ? (int64_t)(rs / spb) * spb * RPT + (int64_t)j * spb + rs % spb
+                             : (int64_t)rs + (int64_t)j * slots;
       if (row >= M) break;
       uint16_t* co = cos_out + row * ldc;
       uint16_t* so = sin_out + row * ldc;
@@ -195,11 +203,14 @@ hipError_t launch_k1_rope(const int64_t* pos, int64_t spos, const float* invf, i
                      (reinterpret_cast<uintptr_t>(cos_out) & 15) == 0 &&
                      (reinterpret_cast<uintptr_t>(sin_out) & 15) == 0 && ldc % 8 == 0 &&
                      N % 8 == 0;
-  const int64_t slots = ((int64_t)M + kRopeRows - 1) / kRopeRows;
-  const int64_t threads = slots * ((N + 7) / 8);
+  const int64_t groups = (N + 7) / 8;
+  const uint32_t spb = groups <= 256 && 256 % groups == 0 ? (uint32_t)(256 / groups) : 0;
+  const int64_t slots = spb ? ((int64_t)M + spb * kRopeRows - 1) / (spb * kRopeRows) * spb
+                            : ((int64_t)M + kRopeRows - 1) / kRopeRows;
+  const int64_t threads = slots * groups;
   if (threads >= (int64_t(1) << 32)) return hipErrorInvalidValue;  // 32-bit thread index
   hipLaunchKernelGGL(k1_rope_kernel<kRopeRows>, dim3(grid_for(threads)), dim3(256), 0, s, pos,
-                     spos, invf, sinv, M, N, cos_out, sin_out, ldc, vec_ok);
+                     spos, invf, sinv, M, N, cos_out, sin_out, ldc, vec_ok, spb);
   return hipGetLastError();
 }
 
