@@ -24,9 +24,12 @@ __device__ __forceinline__ float exp_f(float x) { return exp2f(x * kLog2eF); }
 
 // Workgroup = 64 rows x 16 parts; wave q takes part q, the blocks t = q,
 // q+16, q+32, ..., for 64 consecutive rows (one 256-byte load per block).
-// Two passes instead of a chain of pairwise merges: the row max over every
-// non-empty block, then the sum of s_t * exp(m_t - max), whose exponentials
-// are independent of each other.  Each part adds its blocks in ascending t
+// The first kCombCache blocks of a part (every block up to N = 32768 with
+// 128-column blocks) are loaded at once, both arrays unconditionally, and
+// kept in registers for both passes: the kernel waits for memory about
+// once instead of once per block.  Two passes instead of a chain of
+// pairwise merges: the row max over every non-empty block, then the sum of
+// s_t * exp(m_t - max), whose exponentials are independent of each other.  Each part adds its blocks in ascending t
 // and the sixteen part sums are added in ascending part order: a fixed order,
 // so the result is deterministic.  A block with s == 0 holds no column and
 // is skipped; a block whose sum is NaN (a NaN logit, or exp(inf - inf))
@@ -34,7 +37,7 @@ __device__ __forceinline__ float exp_f(float x) { return exp2f(x * kLog2eF); }
 // This is the pairwise (m, s) (+) (m', s') = (M, s e^{m-M} + s' e^{m'-M})
 // merge unrolled: any order of merges gives the same max and, up to
 // rounding, the same sum.
-constexpr int kCombRows = 64, kCombParts = 16;
+constexpr int kCombRows = 64, kCombParts = 16, kCombCache = 16;
 __global__ void __launch_bounds__(kCombRows * kCombParts) ce_combine_kernel(
     const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ ylab,
     const int32_t* __restrict__ labels, int M, int N, int nblk, float* __restrict__ loss,
@@ -46,12 +49,26 @@ __global__ void __launch_bounds__(kCombRows * kCombParts) ce_combine_kernel(
   const bool live = row < M;
   float m = -INFINITY;
   int nan_seen = 0;
+  float cm[kCombCache], cs[kCombCache];
+#pragma unroll
+  for (int u = 0; u < kCombCache; ++u) {
+    const int t = q + u * kCombParts;
+    const bool ok = live && t < nblk;
+    const int64_t i = (int64_t)t * M + row;
+    cs[u] = ok ? ps[i] : 0.f;
+    cm[u] = ok ? pm[i] : 0.f;
+  }
+#pragma unroll
+  for (int u = 0; u < kCombCache; ++u) {
+    if (cs[u] > 0.f) m = fmaxf(m, cm[u]);
+    else if (cs[u] != cs[u]) nan_seen = 1;
+  }
   if (live) {
 #pragma unroll 4
-    for (int t = q; t < nblk; t += kCombParts) {
+    for (int t = q + kCombCache * kCombParts; t < nblk; t += kCombParts) {
       const int64_t i = (int64_t)t * M + row;
-      const float st = ps[i];
-      if (st > 0.f) m = fmaxf(m, pm[i]);
+      const float st = ps[i], mt = pm[i];
+      if (st > 0.f) m = fmaxf(m, mt);
       else if (st != st) nan_seen = 1;
     }
   }
@@ -67,12 +84,15 @@ __global__ void __launch_bounds__(kCombRows * kCombParts) ce_combine_kernel(
   }
   __syncthreads();
   float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < kCombCache; ++u)
+    if (cs[u] > 0.f) sum += cs[u] * exp_f(cm[u] - mx);
   if (live) {
 #pragma unroll 4
-    for (int t = q; t < nblk; t += kCombParts) {
+    for (int t = q + kCombCache * kCombParts; t < nblk; t += kCombParts) {
       const int64_t i = (int64_t)t * M + row;
-      const float st = ps[i];
-      if (st > 0.f) sum += st * exp_f(pm[i] - mx);
+      const float st = ps[i], mt = pm[i];
+      if (st > 0.f) sum += st * exp_f(mt - mx);
     }
   }
   red[q][r] = sum;
