@@ -161,6 +161,26 @@ __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restric
 //   MODE 2 (many chunks, under 16 outputs): a workgroup per output; thread t
 //     adds chunks t, t+256, ..., then the 256 sums are folded pairwise in a
 //     fixed tree.
+// 0 + partial[kc*L + r] + ... for kc = kc0, kc0 + step, ... < nkc, added in
+// that order.  Eight loads are issued before the first addition waits, so a
+// thread waits for memory once per eight chunks, not once per chunk.
+__device__ __forceinline__ float add_strided(const float* __restrict__ partial, int L, int64_t r,
+                                             int kc0, int step, int nkc) {
+  float t = 0.f;
+  for (int base = kc0; base < nkc; base += 8 * step) {
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int kc = base + u * step;
+      v[u] = kc < nkc ? partial[(int64_t)kc * L + r] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      if (base + u * step < nkc) t += v[u];
+  }
+  return t;
+}
+
 template <int MODE>
 __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ partial, int L,
                                                       int nkc, void* __restrict__ C, int64_t sc,
@@ -171,7 +191,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     __shared__ float red[256];
     r = blockIdx.x;
     float t = 0.f;
-    for (int kc = threadIdx.x; kc < nkc; kc += 256) t += partial[(int64_t)kc * L + r];
+    t = add_strided(partial, L, r, (int)threadIdx.x, 256, nkc);
     red[threadIdx.x] = t;
     __syncthreads();
     for (int w = 128; w > 0; w >>= 1) {
@@ -185,8 +205,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     const int j = threadIdx.x & 15, q = threadIdx.x >> 4;
     r = (int64_t)blockIdx.x * 16 + j;
     float t = 0.f;
-    if (r < L)
-      for (int kc = q; kc < nkc; kc += 16) t += partial[(int64_t)kc * L + r];
+    if (r < L) t = add_strided(partial, L, r, q, 16, nkc);
     red[q][j] = t;
     __syncthreads();
     if (q != 0 || r >= L) return;
@@ -197,7 +216,7 @@ __global__ void __launch_bounds__(256) combine_kernel(const float* __restrict__ 
     r = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (r >= L) return;
     s = 0.f;
-    for (int kc = 0; kc < nkc; ++kc) s += partial[(int64_t)kc * L + r];
+    s = add_strided(partial, L, r, 0, 1, nkc);
   }
   store_out(C, r * sc, s, out_f32);
 }
