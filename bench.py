@@ -81,6 +81,20 @@ def time_stream(fn, steps, warmup, rotate, probe=None):
     return start.elapsed_time(end) / steps
 
 
+def step_times(fn, steps, rotate):
+    """Per-call ms for ``steps`` calls, one HIP event between consecutive
+    calls on the current stream (a separate pass, after the timed region)."""
+    import torch
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record()
+    for i in range(steps):
+        fn(i % rotate)
+        ev[i + 1].record()
+    torch.cuda.synchronize()
+    return [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle as it stands, on the host, on a bounded sample of the NT
     workload: whole output rows of op(A).op(B) for the first rows of X."""
@@ -325,6 +339,13 @@ def main():
         f"idle, {sclk_end:.2f} GHz at the end of the timed steps")
     secondary = {}
     if not args.only_nt:
+        # the same steps once more, right after the timed ones (so at the
+        # sustained clock), with one event between calls: the spread of the
+        # per-step times (median, min, max)
+        per = sorted(step_times(nt_step, K_, copies))
+        secondary["nt_step_us_median"] = round(per[len(per) // 2] * 1e3, 2)
+        secondary["nt_step_us_min"] = round(per[0] * 1e3, 2)
+        secondary["nt_step_us_max"] = round(per[-1] * 1e3, 2)
         # the same operands every step (they stay in the last-level cache)
         ms_warm = time_stream(lambda i: nt_step(0), K_, W_, 1)
         secondary["nt_same_inputs_us"] = round(ms_warm * 1e3, 2)

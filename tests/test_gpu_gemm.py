@@ -91,6 +91,37 @@ def test_tile_configs_agree(M, N, K):
     assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
+def _spread_rows(X, ld):
+    """X [rows, cols] copied into device memory with row stride ``ld``
+    elements (only the first ``cols`` of each stride are written or read)."""
+    rows, cols = X.shape
+    flat = torch.empty((rows - 1) * ld + cols, dtype=X.dtype, device=dev())
+    view = flat.as_strided((rows, cols), (ld, 1))
+    view.copy_(X.to(dev()))
+    return view
+
+
+@pytest.mark.parametrize("ta,tb", [("N", "T"), ("T", "N")])
+def test_leading_dimension_past_2_pow_23(ta, tb):
+    # row strides of 2^23 + 64 elements (16 MiB rows, 2-5 GB per operand):
+    # the tiles leave the 32-bit-offset buffer loads for the bounds-checked
+    # loop with 64-bit addressing; integer-valued entries make the result
+    # exact, so it must equal the oracle and the compact layout bit for bit
+    M, N, K = 300, 130, 200
+    big = (1 << 23) + 64
+    d = workloads.random_operands(M, N, K, ta, tb, seed=23, int_range=4)
+    compact = run_store(d, ta, tb, M, N, K, out_dtype=torch.float32)
+    A = _spread_rows(d["A"], big)
+    B = _spread_rows(d["B"], big)
+    C = torch.full((M, N), float("nan"), dtype=torch.float32, device=dev())
+    tgemm.run(ta, tb, M, N, K, A, big, B, big, C, N, tgemm.EPI_STORE_F32)
+    torch.cuda.synchronize()
+    del A, B
+    ref = oracle_gemm_from(d, ta, tb, M, N, K)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
+    assert torch.equal(C, compact)
+
+
 def test_identity_gives_op_b():
     K = N = 136
     eye = torch.eye(K, dtype=torch.bfloat16)
