@@ -39,12 +39,15 @@ extern "C" int tgemm_clock_probe(int64_t ticks, uint64_t* out_ticks, void* strea
   if (ticks < 1 || ticks > 10000000 || out_ticks == nullptr ||
       (reinterpret_cast<uintptr_t>(out_ticks) & 7) != 0)
     return TGEMM_ERR_INVALID_ARG;
+  // the rate of the device the stream belongs to (the null stream: the
+  // current device)
   int dev = 0, khz = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return TGEMM_ERR_HIP;
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if ((st == nullptr ? hipGetDevice(&dev) : hipStreamGetDevice(st, &dev)) != hipSuccess)
+    return TGEMM_ERR_HIP;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
     return TGEMM_ERR_HIP;
-  hipLaunchKernelGGL(tgemm::clock_probe_kernel, dim3(1), dim3(64), 0,
-                     reinterpret_cast<hipStream_t>(stream), out_ticks, (uint64_t)ticks,
-                     (uint64_t)khz * 1000u);
+  hipLaunchKernelGGL(tgemm::clock_probe_kernel, dim3(1), dim3(64), 0, st, out_ticks,
+                     (uint64_t)ticks, (uint64_t)khz * 1000u);
   return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 }
