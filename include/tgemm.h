@@ -149,8 +149,9 @@ TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int
  * finite e4m3fn value and cast to e4m3fn, and the page's pattern also
  * writes a transposed copy of the fp8 tensor.  Here the GEMM's loader
  * applies the scale, clamp and cast to each element as it reads the bf16
- * operand in its stored layout: no fp8 tensor and no transposed copy is
- * ever written.)
+ * operand in its stored layout, or, for large products, a pass casts each
+ * operand once into a workspace copy in its own layout: no transposed copy
+ * is ever written.)
  *
  *   transA, transB, M, N, K, A, lda, B, ldb, C, ldc: as for tgemm_run with
  *                   a STORE epilogue; A and B are bf16 in any layout.
@@ -167,9 +168,17 @@ TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int
  * 1 / (scale_a * scale_b) to undo both casts.  The products run on the
  * bf16 matrix cores, which hold every e4m3fn value exactly.
  *
- * Validation, errors, asynchrony and streams as for tgemm_run.  Needs no
- * workspace.  Returns TGEMM_OK or a negative tgemm_status; an unsupported
- * epilogue or a NULL `scales` is TGEMM_ERR_INVALID_ARG.
+ * Large products (at least two 256-row and two 256-column tiles, every
+ * stored row 16-byte aligned with a multiple of 8 elements) may instead
+ * cast each operand once, with the same arithmetic, into a compact bf16
+ * copy in its own layout (never transposed) in the library's per-stream
+ * workspace, and multiply the copies: the same bits, fewer casts.  See
+ * tgemm_set_fp8_cast_once.
+ *
+ * Validation, errors, asynchrony and streams as for tgemm_run.  Returns
+ * TGEMM_OK or a negative tgemm_status; an unsupported epilogue or a NULL
+ * `scales` is TGEMM_ERR_INVALID_ARG; TGEMM_ERR_NO_MEMORY if the workspace
+ * for the cast copies cannot be allocated.
  */
 TGEMM_API int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
                   const void* A, int64_t lda, const void* B, int64_t ldb,
@@ -204,6 +213,17 @@ TGEMM_API int tgemm_set_tile_config(int config);
  * 0..64.  Not thread-safe with concurrent tgemm_run calls.
  */
 TGEMM_API int tgemm_set_split_k(int split);
+
+/*
+ * Tuning / testing knob for tgemm_run_fp8: 1 (default) lets large products
+ * (at least two 256-row and two 256-column tiles, 16-byte rows) cast each
+ * operand once, in a pass of its own, into a compact copy in its own layout
+ * in the library's per-stream workspace, before the GEMM; 0 always casts
+ * on load.  Both routes give the same bits.  Returns the previous value,
+ * or TGEMM_ERR_INVALID_ARG for anything but 0 or 1.  Not thread-safe with
+ * concurrent tgemm_run_fp8 calls.
+ */
+TGEMM_API int tgemm_set_fp8_cast_once(int enable);
 
 /*
  * Measurement aid, beside the GEMM path: the shader clock the device runs

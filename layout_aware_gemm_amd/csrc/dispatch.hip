@@ -14,6 +14,7 @@ namespace {
 
 int g_forced_tile = kTileAuto;
 int g_forced_split = 0;
+int g_fp8_cast_once = 1;  // tgemm_set_fp8_cast_once
 
 inline bool is_n(char t) { return t == 'N' || t == 'n'; }
 
@@ -161,6 +162,13 @@ extern "C" int tgemm_set_split_k(int split) {
   if (split < 0 || split > 64) return TGEMM_ERR_INVALID_ARG;
   const int prev = g_forced_split;
   g_forced_split = split;
+  return prev;
+}
+
+extern "C" int tgemm_set_fp8_cast_once(int enable) {
+  if (enable != 0 && enable != 1) return TGEMM_ERR_INVALID_ARG;
+  const int prev = g_fp8_cast_once;
+  g_fp8_cast_once = enable;
   return prev;
 }
 
@@ -335,9 +343,15 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   return status_of(e);
 }
 
-// fp8 (e4m3fn) operands cast on load: every shape runs on the GEMM kernel's
-// register path (the direct copies would move raw bf16); no K split, no
-// matrix-vector or K = 1 shortcut, so every element goes through the cast.
+// fp8 (e4m3fn) operands.  No K split, no matrix-vector or K = 1 shortcut:
+// every element goes through the cast.  Two routes with the same bits:
+//  - cast on load, on the GEMM kernel's register path (the direct copies
+//    would move raw bf16);
+//  - cast once: when both tile counts are at least 2 (so the loader would
+//    cast each element at least twice) and the operands allow 16-byte rows,
+//    a pass casts each operand into a compact copy in its own layout in the
+//    per-stream workspace, and the GEMM reads the copies as plain bf16 (the
+//    direct copies for K-contiguous operands) and applies the output scale.
 extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
                              const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                              int64_t ldc, int epilogue, const float* scales, void* stream) {
@@ -371,10 +385,36 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
               lda % 8 == 0 && ldb % 8 == 0;
   p.C = C;
   p.qscales = scales;
+  const bool bf16_out = epilogue == TGEMM_EPI_STORE_BF16;
+  const int64_t rowsA = is_n(transA) ? M : K, colsA = is_n(transA) ? K : M;
+  const int64_t rowsB = is_n(transB) ? K : N, colsB = is_n(transB) ? N : K;
+  const bool cast_once = g_fp8_cast_once && p.aligned && colsA % 8 == 0 && colsB % 8 == 0 &&
+                         ceil_div(M, 256) >= 2 && ceil_div(N, 256) >= 2;
   if (verbose())
-    fprintf(stderr, "tgemm: fp8 gemm %c%c M=%lld N=%lld K=%lld tile=%d grid=%dx%d aligned=%d\n",
+    fprintf(stderr,
+            "tgemm: fp8 gemm %c%c M=%lld N=%lld K=%lld tile=%d grid=%dx%d aligned=%d "
+            "cast_once=%d\n",
             transA, transB, (long long)M, (long long)N, (long long)K, cfg, p.tilesM, p.tilesN,
-            p.aligned);
-  return status_of(launch_gemm(transA, transB, cfg,
-                               epilogue == TGEMM_EPI_STORE_BF16 ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
+            p.aligned, cast_once ? 1 : 0);
+  if (!cast_once)
+    return status_of(
+        launch_gemm(transA, transB, cfg, bf16_out ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
+  // the two copies, B's at a 256-byte boundary
+  const size_t bytesA = (size_t)rowsA * (size_t)colsA * 2;
+  const size_t offB = (bytesA + 255) / 256 * 256;
+  Workspace w;
+  if (!get_workspace(s, offB + (size_t)rowsB * (size_t)colsB * 2, &w)) return TGEMM_ERR_NO_MEMORY;
+  uint16_t* qa = static_cast<uint16_t*>(w.ptr);
+  uint16_t* qb = reinterpret_cast<uint16_t*>(static_cast<char*>(w.ptr) + offB);
+  hipError_t e = launch_q8_cast(p.A, lda, rowsA, colsA, scales, qa, s);
+  if (e == hipSuccess) e = launch_q8_cast(p.B, ldb, rowsB, colsB, scales + 1, qb, s);
+  if (e == hipSuccess) {
+    p.A = qa;
+    p.B = qb;
+    p.lda = colsA;
+    p.ldb = colsB;
+    e = launch_gemm(transA, transB, cfg, bf16_out ? kEpiOsBf16 : kEpiOsF32, p, s);
+  }
+  const hipError_t r = release_workspace(w, s);
+  return status_of(e != hipSuccess ? e : r);
 }

@@ -799,19 +799,20 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
                                          int n0, int wr0, int wc0, int pcol, uint16_t* lds,
                                          int tid, int lane) {
   const int h = lane >> 5, lc = lane & 31;
-  constexpr bool Q8 = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32;
-  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32 || Q8) {
-    // (Q8: the sum times the output scale, one fp32 multiply)
+  // (Q8, OS: the sum times the output scale, one fp32 multiply)
+  constexpr bool OS = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32 || EPI == kEpiOsBf16 ||
+                      EPI == kEpiOsF32;
+  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32 || OS) {
     float os = 1.f;
-    if constexpr (Q8) os = p.qscales[2];
+    if constexpr (OS) os = p.qscales[2];
     // One output row at a time: its address is formed once, and the FN
     // column blocks of the row are immediate offsets from it.  A wave whose
     // whole block lies inside C stores without bounds tests.
     const int col0 = n0 + wc0 + lc;
     const bool full = m0 + wr0 + 32 * FM <= p.M && n0 + wc0 + 32 * FN <= p.N;
     auto put = [&](int64_t off, float v) __attribute__((always_inline)) {
-      if constexpr (Q8) v = __fmul_rn(v, os);
-      if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16)
+      if constexpr (OS) v = __fmul_rn(v, os);
+      if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16 || EPI == kEpiOsBf16)
         reinterpret_cast<uint16_t*>(p.C)[off] = to_bf16(v);
       else
         reinterpret_cast<float*>(p.C)[off] = v;
@@ -1243,7 +1244,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
 
   __syncthreads();  // every wave is done with LDS (the CE epilogue reuses it)
-  if constexpr (EPI != kEpiCE && !Q8) {
+  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32) {
     if (p.splitk > 1) {
       // K chunk ks of a split product: its fp32 partial goes to slice ks of
       // the workspace; a second kernel adds the slices in chunk order.
@@ -1275,6 +1276,12 @@ hipError_t launch_gemm_tpl(int epi, const GemmParams& p, hipStream_t s) {
       break;
     case kEpiQ8F32:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiQ8F32>), grid, block, 0, s, p);
+      break;
+    case kEpiOsBf16:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiOsBf16>), grid, block, 0, s, p);
+      break;
+    case kEpiOsF32:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiOsF32>), grid, block, 0, s, p);
       break;
     default:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiCE>), grid, block, 0, s, p);

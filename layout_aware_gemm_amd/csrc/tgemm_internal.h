@@ -9,13 +9,17 @@ namespace tgemm {
 
 // Epilogue variants of the matrix-core GEMM kernel.  The Q8 stores take
 // operands cast to e4m3fn on load (scale, clamp, round) and multiply the
-// sum by the output scale before storing.
+// sum by the output scale before storing.  The OS stores multiply by the
+// output scale too, on operands that a separate pass already cast
+// (launch_q8_cast), so their loads are plain bf16.
 enum EpiKind : int {
   kEpiStoreBf16 = 0,
   kEpiStoreF32 = 1,
   kEpiCE = 2,
   kEpiQ8Bf16 = 3,
-  kEpiQ8F32 = 4
+  kEpiQ8F32 = 4,
+  kEpiOsBf16 = 5,
+  kEpiOsF32 = 6
 };
 
 // Tile configurations of the GEMM kernels (k-step 64):
@@ -92,5 +96,11 @@ hipError_t launch_k1_outer_f32(const float* a, int64_t sa, const float* b, int64
                                int N, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_k1_outer_bf16(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb,
                                 int M, int N, void* C, int64_t ldc, bool out_f32, hipStream_t s);
+
+// e4m3fn cast (scale[0], clamp, round; the values kept as bf16) of a
+// row-major [rows, cols] operand with row stride ld into a compact
+// [rows, cols] copy.  X 16-byte aligned, ld % 8 == 0, cols % 8 == 0.
+hipError_t launch_q8_cast(const uint16_t* X, int64_t ld, int64_t rows, int64_t cols,
+                          const float* scale, uint16_t* out, hipStream_t s);
 
 }  // namespace tgemm

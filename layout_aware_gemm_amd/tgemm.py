@@ -31,7 +31,7 @@ EPI_ROPE_COSSIN = 4
 
 EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
            "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k",
-           "tgemm_clock_probe", "tgemm_version")
+           "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version")
 
 
 class TgemmError(RuntimeError):
@@ -72,6 +72,8 @@ def lib():
         L.tgemm_set_tile_config.restype = ctypes.c_int
         L.tgemm_set_split_k.argtypes = [ctypes.c_int]
         L.tgemm_set_split_k.restype = ctypes.c_int
+        L.tgemm_set_fp8_cast_once.argtypes = [ctypes.c_int]
+        L.tgemm_set_fp8_cast_once.restype = ctypes.c_int
         L.tgemm_clock_probe.argtypes = [i64, vp, vp]
         L.tgemm_clock_probe.restype = ctypes.c_int
         L.tgemm_version.argtypes = []
@@ -161,6 +163,16 @@ def set_split_k(split):
     r = lib().tgemm_set_split_k(int(split))
     if r < 0:
         raise TgemmError(r, "tgemm_set_split_k")
+    return r
+
+
+def set_fp8_cast_once(enable):
+    """1 (default): large fp8 products cast each operand once, in a pass of
+    its own, before the GEMM; 0: always cast on load.  Returns the previous
+    setting."""
+    r = lib().tgemm_set_fp8_cast_once(int(enable))
+    if r < 0:
+        raise TgemmError(r, "tgemm_set_fp8_cast_once")
     return r
 
 

@@ -149,3 +149,11 @@ def test_clock_probe_rejects_before_touching_the_gpu():
     assert L.tgemm_clock_probe(0, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
     assert L.tgemm_clock_probe(10 ** 7 + 1, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
     assert L.tgemm_clock_probe(2000, 20, None) == tgemm.TGEMM_ERR_INVALID_ARG
+
+
+def test_set_fp8_cast_once_roundtrip():
+    prev = tgemm.set_fp8_cast_once(0)
+    assert prev == 1
+    assert tgemm.set_fp8_cast_once(prev) == 0
+    with pytest.raises(tgemm.TgemmError):
+        tgemm.set_fp8_cast_once(2)

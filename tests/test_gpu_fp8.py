@@ -117,6 +117,65 @@ def test_nan_propagates_through_the_cast():
         assert within_f32_bound(C[ok].astype(np.float64), ref[ok], absprod[ok], K)
 
 
+# at least two 256-row and two 256-column tiles, every stored row a multiple
+# of 8 elements: these take the cast-once route (a cast pass into a compact
+# copy, then the GEMM on plain bf16) unless it is switched off
+CAST_ONCE = [(600, 520, 1000), (520, 536, 136), (1024, 768, 512)]
+
+
+def run_route(d, ta, tb, M, N, K, scales, cast_once, **kw):
+    prev = tgemm.set_fp8_cast_once(cast_once)
+    try:
+        return run(d, ta, tb, M, N, K, scales, **kw)
+    finally:
+        tgemm.set_fp8_cast_once(prev)
+
+
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("M,N,K", CAST_ONCE)
+def test_cast_once_route(M, N, K, ta, tb):
+    """Integer-valued inputs: the oracle's bits.  Random inputs: the same
+    bits as casting on load, in fp32 and bf16, and within the fp32 bound."""
+    d = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K, int_range=8)
+    assert d["lda"] % 8 == 0 and d["ldb"] % 8 == 0
+    scales = (0.5, 2.0, 0.25)
+    C = run_route(d, ta, tb, M, N, K, scales, 1)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), ref_of(d, ta, tb, M, N, K, scales))
+    r = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K + 1, std=3.0)
+    scales = (4.0, 8.0, 1.0 / 32)
+    for dt in (torch.float32, torch.bfloat16):
+        once = run_route(r, ta, tb, M, N, K, scales, 1, out_dtype=dt)
+        load = run_route(r, ta, tb, M, N, K, scales, 0, out_dtype=dt)
+        if dt == torch.bfloat16:
+            assert np.array_equal(bits(once), bits(load))
+        else:
+            assert torch.equal(once, load)
+    rows = [0, 1, M // 2, M - 1]
+    once_f32 = run_route(r, ta, tb, M, N, K, scales, 1)
+    ref = ref_of(r, ta, tb, M, N, K, scales, rows=rows)
+    absprod = abs_products(r, ta, tb, M, N, K, scales, rows=rows)
+    assert within_f32_bound(once_f32.cpu().numpy()[rows].astype(np.float64), ref, absprod, K)
+
+
+def test_cast_once_keeps_nan():
+    """A NaN element survives the cast pass: its row and column are NaN, the
+    rest equals the cast-on-load route bit for bit."""
+    M, N, K = 520, 536, 256
+    d = workloads.random_operands(M, N, K, "N", "T", seed=41, std=2.0)
+    opA, opB = d["opA"].clone(), d["opB"].clone()
+    opA[5, 3] = float("nan")
+    opB[9, 300] = float("nan")
+    sa_, lda = workloads.store_operand(opA, "N")
+    sb_, ldb = workloads.store_operand(opB, "T")
+    d2 = {"opA": opA, "opB": opB, "A": sa_, "lda": lda, "B": sb_, "ldb": ldb}
+    once = run_route(d2, "N", "T", M, N, K, (1.0, 1.0, 1.0), 1)
+    load = run_route(d2, "N", "T", M, N, K, (1.0, 1.0, 1.0), 0)
+    nan = torch.isnan(once)
+    assert nan[5, :].all() and nan[:, 300].all() and int(nan.sum()) == M + N - 1
+    assert torch.equal(torch.isnan(load), nan)
+    assert torch.equal(once[~nan], load[~nan])
+
+
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_layouts_and_tiles_give_the_same_bits(cfg):
     """The cast happens before the (layout-independent) LDS image, so all
