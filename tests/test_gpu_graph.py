@@ -56,3 +56,32 @@ def test_graph_replays_match_eager():
         assert torch.equal(C, C_ref), rep
         assert torch.equal(loss, loss_ref), rep
         assert torch.equal(grad, grad_ref), rep
+
+
+def test_graph_replays_fp8_cast_once():
+    # 520 x 536 x 256 fp8 product: the cast-once route, whose two cast
+    # passes write into a workspace allocated inside the graph
+    M, N, K = 520, 536, 256
+    d = workloads.random_operands(M, N, K, "N", "T", seed=78, std=3.0)
+    A, B = d["A"].to(dev()), d["B"].to(dev())
+    sc = torch.tensor([4.0, 8.0, 1.0 / 32], dtype=torch.float32, device=dev())
+    C = torch.empty(M, N, dtype=torch.bfloat16, device=dev())
+
+    def call():
+        tgemm.run_fp8("N", "T", M, N, K, A, d["lda"], B, d["ldb"], C, N, tgemm.EPI_STORE_BF16,
+                      sc)
+
+    call()
+    torch.cuda.synchronize()
+    C_ref = C.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for rep in range(3):
+        C.fill_(float("nan"))
+        A.add_(0)                         # eager work on the inputs between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(C, C_ref), rep
