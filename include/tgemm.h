@@ -175,10 +175,12 @@ TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int
  * workspace, and multiply the copies: the same bits, fewer casts.  See
  * tgemm_set_fp8_cast_once.
  *
+ * If the workspace for the copies cannot be allocated, the product casts
+ * on load instead.
+ *
  * Validation, errors, asynchrony and streams as for tgemm_run.  Returns
  * TGEMM_OK or a negative tgemm_status; an unsupported epilogue or a NULL
- * `scales` is TGEMM_ERR_INVALID_ARG; TGEMM_ERR_NO_MEMORY if the workspace
- * for the cast copies cannot be allocated.
+ * `scales` is TGEMM_ERR_INVALID_ARG.
  */
 TGEMM_API int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
                   const void* A, int64_t lda, const void* B, int64_t ldb,

@@ -396,14 +396,14 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
             "cast_once=%d\n",
             transA, transB, (long long)M, (long long)N, (long long)K, cfg, p.tilesM, p.tilesN,
             p.aligned, cast_once ? 1 : 0);
-  if (!cast_once)
-    return status_of(
-        launch_gemm(transA, transB, cfg, bf16_out ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
-  // the two copies, B's at a 256-byte boundary
+  // the two copies, B's at a 256-byte boundary; without the memory for
+  // them the product casts on load instead (same bits, no workspace)
   const size_t bytesA = (size_t)rowsA * (size_t)colsA * 2;
   const size_t offB = (bytesA + 255) / 256 * 256;
   Workspace w;
-  if (!get_workspace(s, offB + (size_t)rowsB * (size_t)colsB * 2, &w)) return TGEMM_ERR_NO_MEMORY;
+  if (!cast_once || !get_workspace(s, offB + (size_t)rowsB * (size_t)colsB * 2, &w))
+    return status_of(
+        launch_gemm(transA, transB, cfg, bf16_out ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
   uint16_t* qa = static_cast<uint16_t*>(w.ptr);
   uint16_t* qb = reinterpret_cast<uint16_t*>(static_cast<char*>(w.ptr) + offB);
   hipError_t e = launch_q8_cast(p.A, lda, rowsA, colsA, scales, qa, s);
