@@ -17,11 +17,12 @@ Everything is computed from the plain definitions in fp64 with NumPy:
                      matmul epilogues" (the attempted fusion: max, shifted
                      exp, sum, log, loss, softmax minus one-hot) and the
                      tile-wise combine its question-and-answer part describes.
-* ``k1_outer`` / ``rope_tables``
-                  -- the K=1 matmul as broadcast-multiply-squeeze and the
-                     permute / duplicate / cos epilogue of "Schedule a small
-                     matmul op as a reduction (or pointwise) op"
-                     (the %kernel_math listing and the proposed decomposition).
+* ``k1_outer`` / ``rope_angles`` / ``rope_tables``
+                  -- the K=1 matmul as one elementwise multiply and the cos /
+                     sin tables of its angles, repeated along the last axis
+                     ("Schedule a small matmul op as a reduction (or
+                     pointwise) op": the %kernel_math listing and the
+                     proposed decomposition).
 * ``bf16``        -- exact bf16 decode and single-rounding round-to-nearest-
                      even encode.
 * ``e4m3_round`` / ``quantize`` / ``gemm_fp8``
@@ -38,8 +39,8 @@ tolerance, because accumulation order on the GPU differs from BLAS's.
 
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
 from .gemm import op_matrix, gemm
-from .xent import cross_entropy, tile_partials, merge_partials, merge_pair
-from .rope import k1_outer, rope_tables
+from .xent import cross_entropy, logsumexp_rows, tile_partials, merge_partials, merge_pair
+from .rope import k1_outer, rope_angles, rope_tables
 from .fp8 import E4M3_MAX, e4m3_round, quantize, gemm_fp8
 
 __all__ = [
@@ -48,10 +49,12 @@ __all__ = [
     "op_matrix",
     "gemm",
     "cross_entropy",
+    "logsumexp_rows",
     "tile_partials",
     "merge_partials",
     "merge_pair",
     "k1_outer",
+    "rope_angles",
     "rope_tables",
     "E4M3_MAX",
     "e4m3_round",

@@ -1,19 +1,26 @@
 """Oracle for the degenerate K=1 matmul and its RoPE epilogue (test infra only).
 
-Follows "Schedule a small matmul op as a reduction (or pointwise) op":
+What is computed ("Schedule a small matmul op as a reduction (or pointwise)
+op": the fusion's inputs and outputs, the %kernel_math listing and the
+proposed decomposition of its K = 1 matmul): the angle of position p and
+frequency i is the fp32 product of the position cast to fp32 and the
+inverse frequency,
 
-* the %kernel_math listing: the [64] inverse frequencies widened to fp32 and
-  broadcast to [1, 64, 1]; the int64 positions [1, 4096] cast to fp32 and
-  broadcast to [1, 1, 4096]; their K=1 matmul giving fp32 [1, 64, 4096];
-  a permute to [1, 4096, 64]; two pads and a cat that duplicate the last
-  dimension to 128; cos; a cast to bf16;
-* the proposed decomposition: that K=1 matmul is a broadcast, an elementwise
-  multiply and a squeeze, i.e. one fp32 multiply per output element.
+    angle[p, i] = fp32(fp32(pos[p]) * inv_freq[i]),
 
-Readings: the pad/pad/cat pair is read as cat(T, T) along the last dimension
-(emb[p, d] = T[p, d mod 64]); the second declared [1, 1, 4096, 128] bf16
-output, whose math the listing cuts off, is read as the sin twin of the cos
-output; the inverse frequencies are taken as fp32 inputs.
+a K = 1 matmul, i.e. one elementwise multiply of two broadcast operands.
+The tables the region emits are cos and sin of those angles, rounded to
+bf16, with the F frequencies repeated once along the last axis:
+
+    cos_table[p, d] = bf16(cos(angle[p, d mod F])),  d < 2F,  likewise sin.
+
+Readings: the two pads and the cat of the listing are read as the last axis
+written twice (table column d holds frequency d mod F); the second declared
+bf16 [4096, 128] output, whose math the listing cuts off after cos, is read
+as the sin table; the inverse frequencies are taken as fp32 inputs.  The
+page multiplies in the order [frequencies] x [positions] and then permutes;
+an fp32 product is exactly rounded and commutes, so the [positions,
+frequencies] product here has the same bits (a pin checks this).
 """
 
 import numpy as np
@@ -32,19 +39,19 @@ def k1_outer(a_f32, b_f32):
     return (a[:, None] * b[None, :]).astype(np.float32)
 
 
-def rope_tables(pos_i64, inv_freq_f32):
-    """Return (T19 fp32 [N, P], emb fp32 [P, 2N], cos bf16 bits, sin bf16 bits).
+def rope_angles(pos_i64, inv_freq_f32):
+    """fp32 angles [P, F]: the position (int64 cast to fp32) times each
+    inverse frequency."""
+    pos32 = np.asarray(pos_i64, dtype=np.int64).reshape(-1).astype(np.float32)
+    return k1_outer(pos32, np.asarray(inv_freq_f32, dtype=np.float32).reshape(-1))
 
-    N = len(inv_freq), P = len(pos).  cos and sin are [P, 2N] uint16 arrays,
-    each the fp64 cos/sin of the fp32 table value rounded once to bf16.
+
+def rope_tables(pos_i64, inv_freq_f32):
+    """Return (angles fp32 [P, F], cos bf16 bits [P, 2F], sin bf16 bits [P, 2F]).
+
+    Each table entry is the fp64 cos / sin of the fp32 angle, rounded once to
+    bf16; column d uses frequency d mod F.
     """
-    pos = np.asarray(pos_i64, dtype=np.int64).reshape(-1)
-    inv_freq = np.asarray(inv_freq_f32, dtype=np.float32).reshape(-1)
-    pos32 = pos.astype(np.float32)                 # int64 -> fp32 cast
-    t19 = k1_outer(inv_freq, pos32)                # [N, P], the page's order
-    t20 = np.ascontiguousarray(t19.T)              # permute -> [P, N]
-    emb = np.concatenate([t20, t20], axis=1)       # duplicate -> [P, 2N]
-    e64 = emb.astype(np.float64)
-    cos_bits = f64_to_bf16_bits(np.cos(e64))
-    sin_bits = f64_to_bf16_bits(np.sin(e64))
-    return t19, emb, cos_bits, sin_bits
+    angles = rope_angles(pos_i64, inv_freq_f32)
+    wide = np.hstack([angles, angles]).astype(np.float64)
+    return angles, f64_to_bf16_bits(np.cos(wide)), f64_to_bf16_bits(np.sin(wide))

@@ -1,17 +1,22 @@
 """Oracle row-wise cross-entropy on GEMM logits (test infrastructure only).
 
-Follows "Allow reductions in matmul epilogues", the attempted fusion, step by
-step and in its order: the fp32 GEMM result y (here fp64, never rounded to
-bf16 first), a one-hot mask from comparing each row's int32 label with the
-column index, the row max m, the shifted exponentials e = exp(y - m) and
-their row sum, lse = log(sum) + m, the per-row loss, and the optional
-softmax-minus-one-hot matrix e / sum - onehot.
+What is computed ("Allow reductions in matmul epilogues", the attempted
+fusion, whose comment defines the loss, and its edit note on the gradient
+kept for the backward pass): for logits y[M, N] and one integer label per
+row,
+
+    loss[m] = logsumexp(y[m, :]) - y[m, label[m]]
+    grad[m, n] = softmax(y[m, :])[n] - [n == label[m]]
+
+written here from those definitions in fp64 (the logits are never rounded
+to bf16 first).  logsumexp is evaluated with the usual shift by the row
+maximum so that large logits neither overflow nor lose the small terms.
 
 Readings where the page is garbled or silent:
 
-* Loss.  The page's comment defines the loss as lse minus the label logit,
-  while its code broadcasts lse across the row before summing (which would
-  give N*lse - y[label]).  The comment and the definition of cross-entropy
+* Loss.  The page's comment gives lse minus the label logit, while its code
+  broadcasts lse across the row before summing (which would give
+  N*lse - y[label]).  The comment and the definition of cross-entropy
   agree, so loss = lse - y[label].  For N = 1 both readings coincide.
 * One loss per row: no mean over rows, no scaling of the gradient, no ignore
   index, no label smoothing.
@@ -29,22 +34,27 @@ sums to the larger max.  The merge identity is (-inf, 0).
 import numpy as np
 
 
+def logsumexp_rows(y):
+    """log(sum_n exp(y[m, n])) for every row m of a 2-D fp64 array."""
+    peak = y.max(axis=1)
+    return peak + np.log(np.exp(y - peak[:, None]).sum(axis=1))
+
+
 def cross_entropy(logits, labels):
     """Return (loss[M], grad[M, N], lse[M]) in fp64 from fp64 logits."""
     y = np.asarray(logits, dtype=np.float64)
     if y.ndim != 2:
         raise ValueError("logits must be [M, N]")
-    M, N = y.shape
-    lab = np.asarray(labels).astype(np.int64).reshape(M)
-    valid = (lab >= 0) & (lab < N)
-    is_label = lab[:, None] == np.arange(N)[None, :]          # one-hot mask
-    m = y.max(axis=1)                                           # row max
-    e = np.exp(y - m[:, None])                                  # shifted exp
-    sumexp = e.sum(axis=1)
-    lse = np.log(sumexp) + m
-    y_label = np.where(is_label, y, 0.0).sum(axis=1)            # the one label logit
-    loss = np.where(valid, lse - y_label, np.nan)
-    grad = e / sumexp[:, None] - is_label.astype(np.float64)
+    n_rows, n_cols = y.shape
+    target = np.asarray(labels).astype(np.int64).reshape(n_rows)
+    lse = logsumexp_rows(y)
+    probs = np.exp(y - lse[:, None])                 # softmax, row by row
+    hit = np.flatnonzero((target >= 0) & (target < n_cols))
+    picked = np.full(n_rows, np.nan)                 # y[m, label[m]] where defined
+    picked[hit] = y[hit, target[hit]]
+    loss = lse - picked
+    grad = probs.copy()
+    grad[hit, target[hit]] -= 1.0                    # minus the one-hot row
     return loss, grad, lse
 
 

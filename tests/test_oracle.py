@@ -298,24 +298,27 @@ def test_k1_outer_is_fp32_product():
 
 def test_rope_tables_structure_and_special_cases():
     w = workloads.rope()
-    t19, emb, cos, sin = oracle.rope_tables(w["pos"].numpy(), w["inv_freq"].numpy())
+    ang, cos, sin = oracle.rope_tables(w["pos"].numpy(), w["inv_freq"].numpy())
     pos = w["pos"].numpy()
     inv = w["inv_freq"].numpy()
-    assert t19.shape == (64, 4096) and emb.shape == (4096, 128)
+    assert ang.shape == (4096, 64) and ang.dtype == np.float32
     assert cos.shape == (4096, 128) and sin.shape == (4096, 128)
-    assert np.array_equal(t19, inv[:, None] * pos.astype(np.float32)[None, :])
-    assert np.array_equal(emb[:, :64], emb[:, 64:])
-    assert np.array_equal(emb[:, :64], t19.T)
+    # the angles are the fp32 products (NumPy's own fp32 multiply)
+    assert np.array_equal(ang, pos.astype(np.float32)[:, None] * inv[None, :])
+    # the page's order ([frequencies] x [positions], then a permute) gives the
+    # same bits: an fp32 product is exactly rounded and commutes
+    assert np.array_equal(oracle.k1_outer(inv, pos.astype(np.float32)).T, ang)
     assert np.array_equal(cos[:, :64], cos[:, 64:]) and np.array_equal(sin[:, :64], sin[:, 64:])
     assert np.all(cos[0] == 0x3F80) and np.all(sin[0] == 0)          # position 0
-    assert inv[0] == 1.0 and np.array_equal(emb[:, 0], pos.astype(np.float32))
+    assert inv[0] == 1.0 and np.array_equal(ang[:, 0], pos.astype(np.float32))
     c = oracle.bf16_bits_to_f64(cos)
     s = oracle.bf16_bits_to_f64(sin)
     assert np.max(np.abs(c * c + s * s - 1)) <= 2 * 2.0 ** -7
     rng = random.Random(0)
     for _ in range(300):
         p, d = rng.randrange(4096), rng.randrange(128)
-        x = float(emb[p, d])
+        x = float(np.float32(float(pos[p])) * np.float32(inv[d % 64]))   # python-side fp32 angle
+        assert x == float(ang[p, d % 64])
         assert abs(py_bf16_to_float(cos[p, d]) - math.cos(x)) <= 2.0 ** -9
         assert abs(py_bf16_to_float(sin[p, d]) - math.sin(x)) <= 2.0 ** -9
 
@@ -339,10 +342,11 @@ def test_golden_page_shapes():
     assert list(flat.shape[:1]) == nt["flattened_input"]["shape"][:1]
     assert flat.data_ptr() == x.data_ptr()            # flattening is a view
     r = g["rope_region"]
-    t19, emb, cos, sin = oracle.rope_tables(workloads.rope()["pos"].numpy(),
-                                            workloads.rope()["inv_freq"].numpy())
-    assert [1] + list(t19.shape) == r["matmul_T19"]["shape"]
-    assert [1] + list(emb.shape) == r["cat_T23"]["shape"]
+    ang, cos, sin = oracle.rope_tables(workloads.rope()["pos"].numpy(),
+                                       workloads.rope()["inv_freq"].numpy())
+    assert [1] + list(ang.T.shape) == r["matmul_T19"]["shape"]
+    assert [1] + list(ang.shape) == r["permute_T20"]["shape"]
+    assert [1] + list(cos.shape) == r["cat_T23"]["shape"]
     assert [1, 1] + list(cos.shape) == r["outputs_T29_T31"]["shape"]
     assert [1, 1] + list(sin.shape) == r["outputs_T29_T31"]["shape"]
     assert list(workloads.rope()["inv_freq"].shape) == r["inv_freq_T3"]["shape"]
