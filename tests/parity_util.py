@@ -11,6 +11,14 @@ GEMM_BF16_TOL = 1e-2     # max |gpu - ref| / (|ref| + 1) for bf16 matrix outputs
 LOSS_REL_TOL = 1e-3      # per-row loss, relative
 K1_F32_ABS_TOL = 1e-5    # K=1 fp32 table, absolute
 TRIG_ABS_TOL = 2.0 ** -8  # bf16 cos/sin tables, absolute (1 bf16 ulp in [0.5, 1))
+# Relative bars scaled to each output's own size.  A bf16 value carries one
+# rounding of at most 2^-9 relative; the gradient carries two (the stored
+# exp(y - block max), then the rescale), so 2^-7 leaves a factor 2 of margin
+# over both, while a wrong value (a uniform or permuted softmax, a scaled
+# product) misses it by far.
+GRAD_REL_TOL = 2.0 ** -7
+GRAD_FLOOR = 2.0 ** -120  # fp32 exponentials of logits ~87 below the row max underflow
+GEMM_REL_TOL = 2.0 ** -8  # max |gpu - ref| / (|ref| + rms(ref)/64) for bf16 products
 
 
 def dev():
@@ -56,3 +64,40 @@ def sample_rows(M, n, seed, tile=128):
     while len(rows) < min(n, M):
         rows.add(int(rng.integers(0, M)))
     return np.array(sorted(rows))
+
+
+def grad_check(g_gpu, grad_ref, labels):
+    """Worst ratio of error to bound (<= 1 passes) of a softmax-minus-one-hot
+    gradient against the oracle's fp64 one.
+
+    Off the label column the probabilities themselves are compared
+    relatively: |g_gpu - g_ref| <= GRAD_REL_TOL * p_ref + GRAD_FLOOR, with
+    p_ref the oracle softmax.  At the label column g = p - 1, whose value
+    carries the roundings of both p and g:
+    |g_gpu - g_ref| <= GRAD_REL_TOL * max(p_ref, |g_ref|) + GRAD_FLOOR.
+    Rows with a label outside [0, N) have no one-hot term.
+    """
+    g = np.asarray(g_gpu, dtype=np.float64)
+    ref = np.asarray(grad_ref, dtype=np.float64)
+    if g.size == 0:
+        return 0.0
+    M, N = ref.shape
+    lab = np.asarray(labels).astype(np.int64).reshape(M)
+    onehot = np.zeros((M, N))
+    hit = np.flatnonzero((lab >= 0) & (lab < N))
+    onehot[hit, lab[hit]] = 1.0
+    p_ref = ref + onehot
+    bound = GRAD_REL_TOL * np.maximum(p_ref, np.abs(ref) * onehot) + GRAD_FLOOR
+    return float(np.max(np.abs(g - ref) / bound))
+
+
+def rms_rel_err(gpu, ref):
+    """max |gpu - ref| / (|ref| + rms(ref)/64): relative for every output not
+    far below the output's typical size, with a floor at 1/64 of its RMS
+    (fp32 accumulation error is orders of magnitude smaller)."""
+    gpu = np.asarray(gpu, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if gpu.size == 0:
+        return 0.0
+    rms = float(np.sqrt(np.mean(ref * ref)))
+    return float(np.max(np.abs(gpu - ref) / (np.abs(ref) + rms / 64.0)))

@@ -11,8 +11,8 @@ import torch
 import oracle
 import workloads
 from layout_aware_gemm_amd import tgemm
-from parity_util import (GEMM_BF16_TOL, bf16_to_f64, bits, dev, oracle_gemm_from, sample_rows,
-                         scaled_err)
+from parity_util import (GEMM_BF16_TOL, GEMM_REL_TOL, bf16_to_f64, bits, dev, oracle_gemm_from,
+                         rms_rel_err, sample_rows, scaled_err)
 
 pytestmark = pytest.mark.gpu
 
@@ -36,7 +36,7 @@ def run_store(d, ta, tb, M, N, K, out_dtype=torch.bfloat16, cfg=0, ldc=None):
     return C
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2])
 @pytest.mark.parametrize("pad", [0, 3])
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", RAGGED)
@@ -70,7 +70,7 @@ def test_integer_valued_bf16_output_is_exact():
     assert np.array_equal(bits(C), oracle.f64_to_bf16_bits(ref))
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3])
+@pytest.mark.parametrize("cfg", [1, 2])
 def test_layouts_bitwise_identical(cfg):
     M, N, K = 384, 320, 448
     outs = []
@@ -83,12 +83,12 @@ def test_layouts_bitwise_identical(cfg):
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 200), (512, 768, 640)])
 def test_tile_configs_agree(M, N, K):
-    # the four-wave 256 / 128 kernels and the eight-wave kernel (interior
-    # tiles on the global->LDS path, edge tiles on the register path) must
-    # produce the same bits
+    # the 256x256 and 128x128 tile kernels (interior tiles on the
+    # global->LDS path, edge tiles on the register path) must produce the
+    # same bits
     d = workloads.random_operands(M, N, K, "N", "T", seed=13)
-    outs = [run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=c) for c in (1, 2, 3)]
-    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+    outs = [run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=c) for c in (1, 2)]
+    assert torch.equal(outs[0], outs[1])
 
 
 def _spread_rows(X, ld):
@@ -162,6 +162,7 @@ def test_nt_down_projection_full_size():
     ref = oracle.gemm("N", "T", 768, 5120, 13824, Xb, 13824, Wb, 13824, rows=rows)
     got = bf16_to_f64(Y.view(768, 5120)[torch.as_tensor(rows, device=dev())])
     assert scaled_err(got, ref) <= GEMM_BF16_TOL
+    assert rms_rel_err(got, ref) <= GEMM_REL_TOL
 
 
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
@@ -177,6 +178,9 @@ def test_layout_sweep_4096(ta, tb):
                       rows=rows)
     got = bf16_to_f64(C[torch.as_tensor(rows, device=dev())])
     assert scaled_err(got, ref) <= GEMM_BF16_TOL
+    # outputs have RMS ~0.016, far below the 1 of the bar above: bound them
+    # relatively too
+    assert rms_rel_err(got, ref) <= GEMM_REL_TOL
     # every layout must give the NT bits
     if (ta, tb) != ("N", "T"):
         sa2, lda2 = workloads.store_operand(w["opA"], "N")

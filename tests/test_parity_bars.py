@@ -1,0 +1,114 @@
+"""The relative parity bars reject plausible wrong answers (CPU only).
+
+Negative controls for the checks the GPU tests apply at the workloads'
+real scales: at the tiny CE (64x256x128) and the fused CE (4096x32000x4096)
+the softmax entries are at most about 1e-2, and the 4096^3 layout-sweep
+outputs have RMS about 0.016, so the absolute-style bar
+max |gpu - ref| / (|ref| + 1) <= 1e-2 alone would pass a gradient that
+ignores the logits or an output scaled by 0.85.  The relative bars must
+fail each such answer and pass the oracle's own values after the roundings
+a correct bf16 result carries.
+"""
+
+import numpy as np
+
+import oracle
+import workloads
+from parity_util import (GEMM_BF16_TOL, GEMM_REL_TOL, grad_check, rms_rel_err, sample_rows,
+                         scaled_err)
+
+
+def onehot_of(labels, N):
+    lab = np.asarray(labels).astype(np.int64)
+    oh = np.zeros((lab.size, N))
+    oh[np.arange(lab.size), lab] = 1.0
+    return oh
+
+
+def wrong_gradients(ref, labels):
+    """Wrong answers that keep every row summing to zero."""
+    M, N = ref.shape
+    oh = onehot_of(labels, N)
+    p = ref + oh
+    return {
+        "uniform": np.full((M, N), 1.0 / N) - oh,                # ignores the logits
+        "permuted": np.roll(p, 1, axis=1) - oh,                  # columns shifted by one
+        "scaled": 0.85 * p - oh * 0.85,                          # wrong scale
+        "sharpened": p ** 1.1 / (p ** 1.1).sum(1, keepdims=True) - oh,  # wrong temperature
+    }
+
+
+def right_gradients(ref, labels):
+    """The oracle's gradient after a correct bf16 result's roundings: once,
+    and with the two roundings' worst case (each probability off by 2^-8
+    relative, in either direction)."""
+    N = ref.shape[1]
+    oh = onehot_of(labels, N)
+    p = ref + oh
+    once = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(ref))
+    up = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(p * (1 + 2.0 ** -8) - oh))
+    down = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(p * (1 - 2.0 ** -8) - oh))
+    return {"once": once, "up": up, "down": down}
+
+
+def check_gradient_bars(y, labels):
+    _, ref, _ = oracle.cross_entropy(y, labels)
+    for name, g in right_gradients(ref, labels).items():
+        assert grad_check(g, ref, labels) <= 1.0, name
+    for name, g in wrong_gradients(ref, labels).items():
+        # the old absolute-style bar is blind to every one of them ...
+        if name in ("uniform", "permuted"):
+            assert scaled_err(g, ref) <= GEMM_BF16_TOL, name
+        # ... the relative one is not
+        assert grad_check(g, ref, labels) > 4.0, name
+
+
+def test_tiny_ce_gradient_bar_rejects_wrong_gradients():
+    w = workloads.tiny_ce()
+    y = oracle.gemm("N", "T", 64, 256, 128, workloads.bf16_bits(w["A"]).reshape(-1), 128,
+                    workloads.bf16_bits(w["W"]).reshape(-1), 128)
+    check_gradient_bars(y, w["labels"].numpy())
+
+
+def test_fused_ce_gradient_bar_rejects_wrong_gradients():
+    w = workloads.ce_vocab()
+    rows = sample_rows(4096, 8, seed=4, tile=1024)
+    y = oracle.gemm("N", "T", 4096, 32000, 4096, workloads.bf16_bits(w["H"]).reshape(-1), 4096,
+                    workloads.bf16_bits(w["W"]).reshape(-1), 4096, rows=rows)
+    check_gradient_bars(y, w["labels"].numpy()[rows])
+
+
+def test_label_column_bar():
+    """At the label column g = p - 1: a label entry that forgot the one-hot
+    term, or subtracted it twice, fails; a probability near 1 is allowed its
+    rounding."""
+    y = np.array([[8.0, 0.0, -1.0, 0.5], [0.0, 0.1, 0.2, 0.3]])
+    labels = np.array([0, 2])
+    _, ref, _ = oracle.cross_entropy(y, labels)
+    ok = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(ref))
+    assert grad_check(ok, ref, labels) <= 1.0
+    bad = ref.copy()
+    bad[1, 2] += 1.0                 # the one-hot term missing
+    assert grad_check(bad, ref, labels) > 4.0
+    bad = ref.copy()
+    bad[0, 0] -= 1.0                 # subtracted twice
+    assert grad_check(bad, ref, labels) > 4.0
+
+
+def test_layout_sweep_bar_rejects_scaled_or_shifted_products():
+    ls = workloads.layout_sweep()
+    sa, lda = workloads.store_operand(ls["opA"], "N")
+    sb, ldb = workloads.store_operand(ls["opB"], "T")
+    rows = sample_rows(4096, 12, seed=3, tile=1024)
+    ref = oracle.gemm("N", "T", 4096, 4096, 4096, workloads.bf16_bits(sa).reshape(-1), lda,
+                      workloads.bf16_bits(sb).reshape(-1), ldb, rows=rows)
+    rounded = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(ref))
+    assert rms_rel_err(rounded, ref) <= GEMM_REL_TOL
+    # a value off by one bf16 step and a half still passes; the bar is not tighter
+    # than the output format
+    assert rms_rel_err(ref * (1 + 2.0 ** -9), ref) <= GEMM_REL_TOL
+    # the absolute-style bar sits near its limit for an output scaled by
+    # 0.85 (about 0.012 against 0.01 on these rows); the relative bar misses
+    # every wrong answer by far
+    for wrong in (0.85 * ref, 0.98 * ref, np.roll(ref, 1, axis=1), ref[::-1]):
+        assert rms_rel_err(wrong, ref) > 4 * GEMM_REL_TOL
