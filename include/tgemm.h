@@ -52,8 +52,10 @@
  *                          matmul, permute, duplicating cat and cos/cast, and
  *                          the proposed broadcast-multiply decomposition.)
  *
- *   Any call with K == 1 and a STORE epilogue runs as a pointwise outer
- *   product (no matrix cores), as that page proposes for K=1 matmuls.
+ *   Every call with K == 1 runs pointwise, without matrix cores, as that
+ *   page proposes for K=1 matmuls: the STORE epilogues as an outer product,
+ *   CE as a per-row reduction of the logits a[m]*b[n] (bf16 operands, the
+ *   products exact in fp32).
  *
  * Errors
  *   Arguments are validated before anything is enqueued; on any error
@@ -72,9 +74,22 @@
  *   a stream run in order and reuse it; it grows with hipFreeAsync /
  *   hipMallocAsync on that stream, so calls on different streams never
  *   share memory.  While `stream` is being captured into a graph the call
- *   allocates and frees its own buffer in stream order instead.  Cached
- *   buffers are held until the process ends.  A stream must not be
- *   destroyed while a tgemm call on it is still executing.
+ *   allocates and frees its own buffer in stream order instead.
+ *
+ * Threads
+ *   tgemm_run may be called from several host threads, on the same stream
+ *   or on different ones.  A call holds its stream's workspace entry from
+ *   the lookup until its last kernel is enqueued, so concurrent calls on
+ *   one stream are enqueued one after the other and never see a buffer
+ *   freed under them.  The tuning knobs (tgemm_set_*) are process-wide and
+ *   must not change while calls are in flight.
+ *
+ * Retention
+ *   A stream's cached buffer is held until the process ends or until
+ *   tgemm_release_workspace(stream) frees it; a program that creates many
+ *   short-lived streams should release each one's buffer before destroying
+ *   the stream.  A stream must not be destroyed while a tgemm call on it is
+ *   still executing.
  */
 #ifndef TGEMM_H
 #define TGEMM_H
@@ -198,9 +213,8 @@ TGEMM_API const char* tgemm_status_string(int status);
 /*
  * Tuning / testing knob: force the GEMM tile configuration for subsequent
  * calls from this process.  0 = automatic (default); 1 = 256x256 tiles;
- * 2 = 128x128 tiles; 3 = 256x256 tiles on the eight-wave kernel (used when
- * A is 'N' and B is 'T', else treated as 1).  Returns the previous value,
- * or TGEMM_ERR_INVALID_ARG for an unknown value.
+ * 2 = 128x128 tiles.  Returns the previous value, or TGEMM_ERR_INVALID_ARG
+ * for an unknown value.
  * Not thread-safe with concurrent tgemm_run calls.
  */
 TGEMM_API int tgemm_set_tile_config(int config);
@@ -210,7 +224,7 @@ TGEMM_API int tgemm_set_tile_config(int config);
  * epilogue is split into (each chunk is a separate workgroup writing an
  * fp32 partial product; a second kernel adds the partials in ascending
  * chunk order, so results do not depend on timing).  Ignored for the CE
- * epilogue and the eight-wave kernel.  0 = automatic (default), 1 = never
+ * epilogue.  0 = automatic (default), 1 = never
  * split.  Returns the previous value, or TGEMM_ERR_INVALID_ARG outside
  * 0..64.  Not thread-safe with concurrent tgemm_run calls.
  */
@@ -241,6 +255,16 @@ TGEMM_API int tgemm_set_fp8_cast_once(int enable);
  * out_ticks; checked before any device call) or TGEMM_ERR_HIP.
  */
 TGEMM_API int tgemm_clock_probe(int64_t ticks, uint64_t* out_ticks, void* stream);
+
+/*
+ * Free the cached workspace buffer of (current device, `stream`) in stream
+ * order (hipFreeAsync on `stream`); the next tgemm_run on that stream
+ * allocates a new one.  Work already enqueued keeps a valid buffer.  A
+ * stream that has none is a no-op.  Must not race with tgemm_run calls on
+ * the same stream from other threads (it waits for a call holding the entry
+ * to finish enqueueing).  Returns TGEMM_OK or TGEMM_ERR_HIP.
+ */
+TGEMM_API int tgemm_release_workspace(void* stream);
 
 /* Library version as MAJOR*10000 + MINOR*100 + PATCH. */
 TGEMM_API int tgemm_version(void);

@@ -3,6 +3,7 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <memory>
 #include <mutex>
 #include <vector>
 
@@ -41,15 +42,13 @@ bool verbose() {
 //    bytes per flop of a 128x128 one, which pays for writing and re-reading
 //    the fp32 partials when every chunk still spans at least 2048 of K.
 //  - Otherwise 128x128 tiles.
-// The eight-wave kernel (kTilePP) and other splits are used only when
-// requested.
+// Other splits are used only when requested.
 int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
   const int64_t t256 = (int64_t)ceil_div(M, 256) * ceil_div(N, 256);
   const bool store = epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32;
   int cfg, s = 1;
   if (g_forced_tile != kTileAuto) {
     cfg = g_forced_tile;
-    if (cfg == kTilePP && !nt) cfg = kTile256;
   } else if (t256 >= 200) {
     cfg = kTile256;
   } else {
@@ -63,7 +62,7 @@ int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
     }
   }
   if (g_forced_split > 0) s = g_forced_split;
-  if (cfg == kTilePP || !store) s = 1;
+  if (!store) s = 1;
   // every chunk holds at least one k-step
   const int max_s = ceil_div(K, 64);
   if (s > max_s) s = max_s;
@@ -73,18 +72,27 @@ int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
 
 int status_of(hipError_t e) { return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP; }
 
-// Workspace (CE partials, split-K partial products), one buffer per
-// (device, stream).  Calls on one stream run in order, so each reuses the
-// buffer the previous call on that stream used; growing it frees the old
-// buffer and allocates the new one in stream order (hipFreeAsync /
-// hipMallocAsync on that stream), so work still queued keeps a valid
-// buffer.  Calls on different streams never share a buffer.  While the
-// stream is being captured into a graph, a call gets a buffer of its own
-// that is freed in stream order at its end (the graph owns it), exactly as
-// if there were no cache.  Cached buffers live until the process ends.
+// ----------------------------------------------------------------------
+// Workspace: the CE partials, the split-K partial products and the gemv
+// partials.
+//
+// tgemm_run: one cached buffer per (device, stream).  Calls on one stream
+// run in order, so each reuses the buffer the previous call on that stream
+// used; growing it frees the old buffer and allocates the new one in
+// stream order (hipFreeAsync / hipMallocAsync on that stream), so work
+// still queued keeps a valid buffer.  A call holds the entry's lock from
+// the lookup until its last kernel is enqueued, so two host threads that
+// share a stream cannot grow (and free) a buffer the other has handed to
+// kernels it has not yet enqueued.  Calls on different streams never share
+// a buffer.  While the stream is being captured into a graph, a call gets a
+// buffer of its own that is freed in stream order at its end (the graph
+// owns it).  Cached buffers live until the process ends or until
+// tgemm_release_workspace.
+// ----------------------------------------------------------------------
 struct Workspace {
-  void* ptr;
-  bool owned;  // free at the end of this call
+  void* ptr = nullptr;
+  bool owned = false;                 // free in stream order at the end of this call
+  std::unique_lock<std::mutex> hold;  // the cache entry, until the last launch is enqueued
 };
 
 struct WsEntry {
@@ -92,57 +100,69 @@ struct WsEntry {
   hipStream_t stream;
   void* ptr;
   size_t bytes;
+  std::mutex mu;
 };
 
-std::mutex g_ws_mu;
-std::vector<WsEntry> g_ws;
+std::mutex g_ws_mu;                               // guards the list itself
+std::vector<std::unique_ptr<WsEntry>> g_ws;       // entries never move or go away
 
-bool get_workspace(hipStream_t s, size_t bytes, Workspace* w) {
+enum WsMode : int { kWsCached = 0 };
+
+// Returns TGEMM_OK with w->ptr set, TGEMM_ERR_NO_MEMORY (allocation
+// failed) or TGEMM_ERR_HIP.
+int get_workspace(WsMode mode, hipStream_t s, size_t bytes, Workspace* w) {
   w->ptr = nullptr;
   w->owned = false;
+  (void)mode;
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (s != nullptr && hipStreamIsCapturing(s, &cs) == hipSuccess &&
       cs != hipStreamCaptureStatusNone) {
     if (hipMallocAsync(&w->ptr, bytes, s) != hipSuccess || w->ptr == nullptr) {
       (void)hipGetLastError();
-      return false;
+      return TGEMM_ERR_NO_MEMORY;
     }
     w->owned = true;
-    return true;
+    return TGEMM_OK;
   }
   (void)hipGetLastError();
   int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return false;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
+  if (hipGetDevice(&dev) != hipSuccess) return TGEMM_ERR_HIP;
   WsEntry* e = nullptr;
-  for (auto& x : g_ws)
-    if (x.dev == dev && x.stream == s) e = &x;
-  if (e != nullptr && e->bytes >= bytes) {
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    for (auto& x : g_ws)
+      if (x->dev == dev && x->stream == s) e = x.get();
+    if (e == nullptr) {
+      g_ws.push_back(std::unique_ptr<WsEntry>(new WsEntry{dev, s, nullptr, 0, {}}));
+      e = g_ws.back().get();
+    }
+  }
+  w->hold = std::unique_lock<std::mutex>(e->mu);
+  if (e->ptr != nullptr && e->bytes >= bytes) {
     w->ptr = e->ptr;
-    return true;
+    return TGEMM_OK;
   }
   // grow by at least a quarter, so a slowly growing size does not
   // reallocate on every call
   size_t want = bytes;
-  if (e != nullptr && want < e->bytes + e->bytes / 4) want = e->bytes + e->bytes / 4;
+  if (e->ptr != nullptr && want < e->bytes + e->bytes / 4) want = e->bytes + e->bytes / 4;
   void* p = nullptr;
   if (hipMallocAsync(&p, want, s) != hipSuccess || p == nullptr) {
     (void)hipGetLastError();
-    return false;
+    w->hold.unlock();
+    return TGEMM_ERR_NO_MEMORY;
   }
-  if (e != nullptr) {
-    (void)hipFreeAsync(e->ptr, s);
-    e->ptr = p;
-    e->bytes = want;
-  } else {
-    g_ws.push_back(WsEntry{dev, s, p, want});
-  }
+  if (e->ptr != nullptr) (void)hipFreeAsync(e->ptr, s);
+  e->ptr = p;
+  e->bytes = want;
   w->ptr = p;
-  return true;
+  return TGEMM_OK;
 }
 
-hipError_t release_workspace(const Workspace& w, hipStream_t s) {
-  return w.owned ? hipFreeAsync(w.ptr, s) : hipSuccess;
+hipError_t release_workspace(Workspace& w, hipStream_t s) {
+  const hipError_t e = w.owned ? hipFreeAsync(w.ptr, s) : hipSuccess;
+  if (w.hold.owns_lock()) w.hold.unlock();
+  return e;
 }
 
 hipError_t launch_gemm(char ta, char tb, int cfg, int epi, const GemmParams& p, hipStream_t s) {
@@ -173,32 +193,61 @@ extern "C" int tgemm_set_fp8_cast_once(int enable) {
 }
 
 extern "C" int tgemm_set_tile_config(int config) {
-  if (config < kTileAuto || config > kTilePP) return TGEMM_ERR_INVALID_ARG;
+  if (config < kTileAuto || config > kTile128) return TGEMM_ERR_INVALID_ARG;
   const int prev = g_forced_tile;
   g_forced_tile = config;
   return prev;
 }
 
-extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t K,
-                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
-                         int64_t ldc, int epilogue, const int32_t* labels, float* out_loss,
-                         void* out_grad, void* stream) {
-  const int st = tgemm_validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
-                                out_loss, out_grad);
-  if (st != TGEMM_OK) return st;
+extern "C" int tgemm_release_workspace(void* stream) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return TGEMM_ERR_HIP;
+  }
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  WsEntry* e = nullptr;
+  {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    for (auto& x : g_ws)
+      if (x->dev == dev && x->stream == s) e = x.get();
+  }
+  if (e == nullptr) return TGEMM_OK;
+  std::lock_guard<std::mutex> hold(e->mu);
+  hipError_t r = hipSuccess;
+  if (e->ptr != nullptr) r = hipFreeAsync(e->ptr, s);
+  e->ptr = nullptr;
+  e->bytes = 0;
+  return status_of(r);
+}
+
+namespace tgemm {
+namespace {
+
+// The whole of tgemm_run after validation, with the workspace taken from
+// `mode`'s source.
+int run_impl(WsMode mode, char transA, char transB, int64_t M, int64_t N, int64_t K,
+             const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
+             int epilogue, const int32_t* labels, float* out_loss, void* out_grad,
+             hipStream_t s) {
   const int m = (int)M, n = (int)N, k = (int)K;
 
   // Element strides of the length-M / length-N vectors of a K=1 product.
   const int64_t sa = is_n(transA) ? lda : 1;
   const int64_t sb = is_n(transB) ? 1 : ldb;
 
-  if (epilogue == TGEMM_EPI_ROPE_COSSIN || epilogue == TGEMM_EPI_OUTER_F32 ||
-      (K == 1 && (epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32))) {
+  if (K == 1) {
+    // Every K = 1 call runs pointwise, without matrix cores.
+    hipError_t e;
+    if (epilogue == TGEMM_EPI_CE) {
+      if (verbose()) fprintf(stderr, "tgemm: K=1 pointwise cross-entropy\n");
+      e = launch_k1_ce(static_cast<const uint16_t*>(A), sa, static_cast<const uint16_t*>(B), sb,
+                       m, n, labels, out_loss, static_cast<uint16_t*>(out_grad), ldc, s);
+      return status_of(e);
+    }
     const int64_t groups = epilogue == TGEMM_EPI_ROPE_COSSIN ? (N + 7) / 8 : (N + 3) / 4;
     if ((M * groups + 255) / 256 > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
     if (verbose()) fprintf(stderr, "tgemm: K=1 pointwise path, epilogue %d\n", epilogue);
-    hipError_t e;
     if (epilogue == TGEMM_EPI_ROPE_COSSIN)
       e = launch_k1_rope(static_cast<const int64_t*>(A), sa, static_cast<const float*>(B), sb, m,
                          n, static_cast<uint16_t*>(C), static_cast<uint16_t*>(out_grad), ldc, s);
@@ -212,7 +261,7 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
     return status_of(e);
   }
 
-  if ((M == 1 || N == 1) && K > 1 &&
+  if ((M == 1 || N == 1) &&
       (epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32)) {
     // Matrix-vector or dot product: HBM-bound reductions, no matrix cores.
     const uint16_t* a = static_cast<const uint16_t*>(A);
@@ -256,7 +305,8 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
       fprintf(stderr, "tgemm: %s M=%d N=%d K=%lld L=%d chunks=%lld\n",
               shape == kGemvRows ? "rowdot" : "colsweep", m, n, (long long)K, L, (long long)nkc);
     Workspace w;
-    if (!get_workspace(s, (size_t)(nkc * L) * sizeof(float), &w)) return TGEMM_ERR_NO_MEMORY;
+    const int ws = get_workspace(mode, s, (size_t)(nkc * L) * sizeof(float), &w);
+    if (ws != TGEMM_OK) return ws;
     hipError_t e = launch_gemv(shape, X, ldx, sx, v, sv, L, K, (int)nkc,
                                static_cast<float*>(w.ptr), C, sc,
                                epilogue == TGEMM_EPI_STORE_F32, s);
@@ -293,18 +343,17 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
             p.aligned, epilogue);
 
   if (epilogue != TGEMM_EPI_CE && split > 1) {
-    // Split-K: one fp32 partial product per chunk, then the sum.
+    // Split-K: one fp32 partial product per chunk (the fp32 store instance
+    // writes it), then the sum in chunk order.
     const size_t ws_bytes = (size_t)split * (size_t)M * (size_t)N * sizeof(float);
     Workspace w;
-    if (!get_workspace(s, ws_bytes, &w)) return TGEMM_ERR_NO_MEMORY;
-    float* ws = static_cast<float*>(w.ptr);
-    p.ws = ws;
+    const int ws = get_workspace(mode, s, ws_bytes, &w);
+    if (ws != TGEMM_OK) return ws;
+    p.ws = static_cast<float*>(w.ptr);
     p.C = C;
-    hipError_t e = launch_gemm(transA, transB, cfg,
-                               epilogue == TGEMM_EPI_STORE_BF16 ? kEpiStoreBf16 : kEpiStoreF32, p,
-                               s);
+    hipError_t e = launch_gemm(transA, transB, cfg, kEpiStoreF32, p, s);
     if (e == hipSuccess)
-      e = launch_splitk_sum(ws, split, m, n, C, ldc, epilogue == TGEMM_EPI_STORE_F32, s);
+      e = launch_splitk_sum(p.ws, split, m, n, C, ldc, epilogue == TGEMM_EPI_STORE_F32, s);
     const hipError_t ef = release_workspace(w, s);
     if (e == hipSuccess) e = ef;
     return status_of(e);
@@ -325,12 +374,13 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   const int nblk = p.tilesN * (tile_cols(cfg) / blk);
   const size_t ws_floats = 2 * (size_t)nblk * M + 2 * (size_t)M;
   Workspace w;
-  if (!get_workspace(s, ws_floats * sizeof(float), &w)) return TGEMM_ERR_NO_MEMORY;
-  float* ws = static_cast<float*>(w.ptr);
+  const int ws = get_workspace(mode, s, ws_floats * sizeof(float), &w);
+  if (ws != TGEMM_OK) return ws;
+  float* wsf = static_cast<float*>(w.ptr);
   p.labels = labels;
-  p.part_m = ws;
-  p.part_s = ws + (size_t)nblk * M;
-  p.ylabel = ws + 2 * (size_t)nblk * M;
+  p.part_m = wsf;
+  p.part_s = wsf + (size_t)nblk * M;
+  p.ylabel = wsf + 2 * (size_t)nblk * M;
   float* lse = p.ylabel + M;
   p.grad = static_cast<uint16_t*>(out_grad);
   hipError_t e = launch_gemm(transA, transB, cfg, kEpiCE, p, s);
@@ -341,6 +391,20 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   const hipError_t ef = release_workspace(w, s);
   if (e == hipSuccess) e = ef;
   return status_of(e);
+}
+
+}  // namespace
+}  // namespace tgemm
+
+extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                         const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                         int64_t ldc, int epilogue, const int32_t* labels, float* out_loss,
+                         void* out_grad, void* stream) {
+  const int st = tgemm_validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
+                                out_loss, out_grad);
+  if (st != TGEMM_OK) return st;
+  return run_impl(kWsCached, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
+                  out_loss, out_grad, reinterpret_cast<hipStream_t>(stream));
 }
 
 // fp8 (e4m3fn) operands.  No K split, no matrix-vector or K = 1 shortcut:
@@ -365,7 +429,6 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
   // of tiles up (measured on 4096x3072x4096: 237 against 248 us).
   int cfg = g_forced_tile;
   if (cfg == kTileAuto) cfg = t256 >= 128 ? kTile256 : kTile128;
-  if (cfg == kTilePP) cfg = kTile256;
   GemmParams p = {};
   p.A = static_cast<const uint16_t*>(A);
   p.B = static_cast<const uint16_t*>(B);
@@ -401,7 +464,8 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
   const size_t bytesA = (size_t)rowsA * (size_t)colsA * 2;
   const size_t offB = (bytesA + 255) / 256 * 256;
   Workspace w;
-  if (!cast_once || !get_workspace(s, offB + (size_t)rowsB * (size_t)colsB * 2, &w))
+  if (!cast_once ||
+      get_workspace(kWsCached, s, offB + (size_t)rowsB * (size_t)colsB * 2, &w) != TGEMM_OK)
     return status_of(
         launch_gemm(transA, transB, cfg, bf16_out ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
   uint16_t* qa = static_cast<uint16_t*>(w.ptr);

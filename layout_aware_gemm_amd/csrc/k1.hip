@@ -192,6 +192,63 @@ __global__ void __launch_bounds__(256) k1_outer_bf16_kernel(
   }
 }
 
+// K = 1 with the cross-entropy epilogue: row m's logits are y[n] = a[m] *
+// b[n] (bf16 operands; the product is exact in fp32), so the row reduction
+// needs no matrix cores either.  One workgroup per row.  Pass 1: the row
+// max; pass 2: the sum of exp(y - max); each thread walks a strided share
+// of the columns in ascending order and the 256 thread values are folded
+// by a fixed tree in LDS, so the result is deterministic.  lse = max +
+// ln(sum), loss = lse - y[label] (NaN for a label outside [0, N)).  With a
+// gradient buffer, pass 3 writes bf16(exp(y - lse) - [n == label]).  A NaN
+// logit makes the sum, and so the loss and the gradient row, NaN.
+constexpr int kCeK1Threads = 256;
+constexpr float kCeLog2e = 1.4426950408889634f;
+constexpr float kCeLn2 = 0.6931471805599453f;
+
+__device__ __forceinline__ float block_fold(float v, float* red, bool is_max) {
+  const int t = threadIdx.x;
+  red[t] = v;
+  __syncthreads();
+#pragma unroll
+  for (int o = kCeK1Threads / 2; o > 0; o >>= 1) {
+    if (t < o) red[t] = is_max ? fmaxf(red[t], red[t + o]) : red[t] + red[t + o];
+    __syncthreads();
+  }
+  const float r = red[0];
+  __syncthreads();
+  return r;
+}
+
+__global__ void __launch_bounds__(kCeK1Threads) k1_ce_kernel(
+    const uint16_t* __restrict__ a, int64_t sa, const uint16_t* __restrict__ b, int64_t sb, int N,
+    const int32_t* __restrict__ labels, float* __restrict__ loss, uint16_t* __restrict__ grad,
+    int64_t ldg) {
+  __shared__ float red[kCeK1Threads];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const float av = from_bf16(a[row * sa]);
+  float mx = -INFINITY;
+  for (int n = t; n < N; n += kCeK1Threads)
+    mx = fmaxf(mx, __fmul_rn(av, from_bf16(b[(int64_t)n * sb])));
+  mx = block_fold(mx, red, true);
+  float sum = 0.f;
+  for (int n = t; n < N; n += kCeK1Threads)
+    sum += exp2f((__fmul_rn(av, from_bf16(b[(int64_t)n * sb])) - mx) * kCeLog2e);
+  sum = block_fold(sum, red, false);
+  const float lse = mx + log2f(sum) * kCeLn2;
+  const int lab = labels[row];
+  const bool valid = lab >= 0 && lab < N;
+  if (t == 0)
+    loss[row] = valid ? lse - __fmul_rn(av, from_bf16(b[(int64_t)lab * sb]))
+                      : __int_as_float(0x7fc00000);
+  if (grad == nullptr) return;
+  uint16_t* g = grad + row * ldg;
+  for (int n = t; n < N; n += kCeK1Threads) {
+    const float y = __fmul_rn(av, from_bf16(b[(int64_t)n * sb]));
+    g[n] = to_bf16(exp2f((y - lse) * kCeLog2e) - (n == lab ? 1.f : 0.f));
+  }
+}
+
 inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 256); }
 
 }  // namespace
@@ -227,6 +284,14 @@ hipError_t launch_k1_outer_bf16(const uint16_t* a, int64_t sa, const uint16_t* b
   const int64_t threads = (int64_t)M * ((N + 3) / 4);
   hipLaunchKernelGGL(k1_outer_bf16_kernel, dim3(grid_for(threads)), dim3(256), 0, s, a, sa, b, sb,
                      M, N, C, ldc, out_f32 ? 1 : 0);
+  return hipGetLastError();
+}
+
+hipError_t launch_k1_ce(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb, int M,
+                        int N, const int32_t* labels, float* loss, uint16_t* grad, int64_t ldg,
+                        hipStream_t s) {
+  hipLaunchKernelGGL(k1_ce_kernel, dim3((unsigned)M), dim3(kCeK1Threads), 0, s, a, sa, b, sb, N,
+                     labels, loss, grad, ldg);
   return hipGetLastError();
 }
 

@@ -22,11 +22,9 @@ enum EpiKind : int {
   kEpiOsF32 = 6
 };
 
-// Tile configurations of the GEMM kernels (k-step 64):
-//   kTile256 / kTile128: BM x BN = 256x256 / 128x128, 4 waves in a 2x2 grid;
-//   kTilePP: 256x256, 8 waves in two ping-pong groups (A and B K-contiguous
-//            only), each wave 128x64.
-enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2, kTilePP = 3 };
+// Tile configurations of the GEMM kernel (k-step 64): BM x BN = 256x256 or
+// 128x128, 4 waves in a 2x2 grid.
+enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2 };
 
 struct GemmParams {
   const uint16_t* A;  // bf16 bits
@@ -96,6 +94,12 @@ hipError_t launch_k1_outer_f32(const float* a, int64_t sa, const float* b, int64
                                int N, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_k1_outer_bf16(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb,
                                 int M, int N, void* C, int64_t ldc, bool out_f32, hipStream_t s);
+// Cross-entropy of the K = 1 logits y[m, n] = a[m] * b[n] (bf16 operands):
+// loss[m] = logsumexp_n y - y[m, labels[m]]; grad (optional, row stride ldg)
+// = bf16(softmax - onehot).  One workgroup per row.
+hipError_t launch_k1_ce(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb, int M,
+                        int N, const int32_t* labels, float* loss, uint16_t* grad, int64_t ldg,
+                        hipStream_t s);
 
 // e4m3fn cast (scale[0], clamp, round; the values kept as bf16) of a
 // row-major [rows, cols] operand with row stride ld into a compact

@@ -80,4 +80,4 @@ extern "C" const char* tgemm_status_string(int status) {
   }
 }
 
-extern "C" int tgemm_version(void) { return 100; }
+extern "C" int tgemm_version(void) { return 200; }

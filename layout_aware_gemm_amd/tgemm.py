@@ -31,7 +31,8 @@ EPI_ROPE_COSSIN = 4
 
 EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
            "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k",
-           "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version")
+           "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version",
+           "tgemm_release_workspace")
 
 
 class TgemmError(RuntimeError):
@@ -78,6 +79,8 @@ def lib():
         L.tgemm_clock_probe.restype = ctypes.c_int
         L.tgemm_version.argtypes = []
         L.tgemm_version.restype = ctypes.c_int
+        L.tgemm_release_workspace.argtypes = [vp]
+        L.tgemm_release_workspace.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -149,8 +152,7 @@ def validate_fp8(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, scal
 
 
 def set_tile_config(cfg):
-    """0 = automatic, 1 = 256x256, 2 = 128x128, 3 = 256x256 eight-wave (NT only);
-    returns the previous setting."""
+    """0 = automatic, 1 = 256x256, 2 = 128x128; returns the previous setting."""
     r = lib().tgemm_set_tile_config(int(cfg))
     if r < 0:
         raise TgemmError(r, "tgemm_set_tile_config")
@@ -174,6 +176,14 @@ def set_fp8_cast_once(enable):
     if r < 0:
         raise TgemmError(r, "tgemm_set_fp8_cast_once")
     return r
+
+
+def release_workspace(stream=None, device=None):
+    """Free (in stream order) the library's cached workspace of ``stream`` on
+    the current device; the next call on that stream allocates afresh."""
+    r = lib().tgemm_release_workspace(_stream(stream, device))
+    if r != TGEMM_OK:
+        raise TgemmError(r, "tgemm_release_workspace")
 
 
 def clock_probe(ticks=2000, out=None, stream=None):
