@@ -111,7 +111,9 @@ typedef enum {
   TGEMM_ERR_INVALID_ARG = -1, /* a flag, size, leading dimension or pointer is invalid */
   TGEMM_ERR_UNSUPPORTED = -2, /* valid request this library does not implement      */
   TGEMM_ERR_HIP = -3,         /* the HIP runtime reported an error while enqueueing   */
-  TGEMM_ERR_NO_MEMORY = -4    /* a CE or split-K workspace could not be allocated     */
+  TGEMM_ERR_NO_MEMORY = -4,   /* a CE or split-K workspace could not be allocated     */
+  TGEMM_ERR_WORKSPACE_LIMIT = -5 /* tgemm_run_noalloc: the call needs more scratch than
+                                    its fixed buffer holds (tgemm_noalloc_scratch_bytes) */
 } tgemm_status;
 
 typedef enum {
@@ -144,6 +146,36 @@ TGEMM_API int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t 
               void* C, int64_t ldc, int epilogue,
               const int32_t* labels, float* out_loss, void* out_grad,
               void* stream);
+
+/*
+ * tgemm_run without allocation, for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, results and errors as tgemm_run (the
+ * same kernels), but every scratch buffer the call needs -- the split-K
+ * partial products, the cross-entropy block partials, the matrix-vector
+ * partials -- lives in one fixed device array of the library,
+ * tgemm_noalloc_scratch_bytes() = 64 MiB per device, held from the first
+ * use on a device until the process ends.  The call makes no hipMalloc,
+ * hipFree or other allocating call; the caller still owns every input and
+ * output.  A call whose scratch need exceeds the array returns
+ * TGEMM_ERR_WORKSPACE_LIMIT before anything is enqueued (the 768x5120x13824
+ * NT product needs 60 MiB; split-K needs 4*chunks*M*N bytes, cross-entropy
+ * about 8*M*(N/128 + 1) bytes).
+ *
+ * Every call on a device shares that device's array, and the array keeps
+ * the last call's contents (no kernel relies on them: each writes every
+ * scratch value it reads).  Calls that may overlap on one device -- on two
+ * streams, or from two threads -- race on the array and give wrong
+ * results; serialise them (one stream, in order) or use tgemm_run.
+ */
+TGEMM_API int tgemm_run_noalloc(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                const void* A, int64_t lda, const void* B, int64_t ldb,
+                                void* C, int64_t ldc, int epilogue,
+                                const int32_t* labels, float* out_loss, void* out_grad,
+                                void* stream);
+
+/* Size in bytes of tgemm_run_noalloc's fixed scratch array. */
+TGEMM_API int64_t tgemm_noalloc_scratch_bytes(void);
 
 /*
  * Host-only argument check with the same rules as tgemm_run, without

@@ -11,6 +11,15 @@
 #include "tgemm_internal.h"
 
 namespace tgemm {
+
+// The no-allocation workspace of tgemm_run_noalloc: 64 MiB of device memory
+// per device, held from the library's first use on that device until the
+// process ends.  Host code never uses the array's name as an address: the
+// device address of each device's copy comes from hipGetSymbolAddress,
+// made once per device with that device current (scratch_address below).
+constexpr size_t kScratchBytes = size_t(64) << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
 namespace {
 
 int g_forced_tile = kTileAuto;
@@ -74,7 +83,7 @@ int status_of(hipError_t e) { return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 
 // ----------------------------------------------------------------------
 // Workspace: the CE partials, the split-K partial products and the gemv
-// partials.
+// partials.  Two sources.
 //
 // tgemm_run: one cached buffer per (device, stream).  Calls on one stream
 // run in order, so each reuses the buffer the previous call on that stream
@@ -88,6 +97,9 @@ int status_of(hipError_t e) { return e == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
 // buffer of its own that is freed in stream order at its end (the graph
 // owns it).  Cached buffers live until the process ends or until
 // tgemm_release_workspace.
+//
+// tgemm_run_noalloc: the fixed device array `scratch` below, one per
+// device, found once per device with hipGetSymbolAddress; no allocation.
 // ----------------------------------------------------------------------
 struct Workspace {
   void* ptr = nullptr;
@@ -106,14 +118,44 @@ struct WsEntry {
 std::mutex g_ws_mu;                               // guards the list itself
 std::vector<std::unique_ptr<WsEntry>> g_ws;       // entries never move or go away
 
-enum WsMode : int { kWsCached = 0 };
+enum WsMode : int { kWsCached = 0, kWsScratch = 1 };
+
+// (the array `scratch` is defined at file scope, below the anonymous
+// namespace)
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return TGEMM_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return TGEMM_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return TGEMM_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return TGEMM_OK;
+}
 
 // Returns TGEMM_OK with w->ptr set, TGEMM_ERR_NO_MEMORY (allocation
-// failed) or TGEMM_ERR_HIP.
+// failed), TGEMM_ERR_WORKSPACE_LIMIT (scratch too small) or TGEMM_ERR_HIP.
 int get_workspace(WsMode mode, hipStream_t s, size_t bytes, Workspace* w) {
   w->ptr = nullptr;
   w->owned = false;
-  (void)mode;
+  if (mode == kWsScratch) {
+    if (bytes > kScratchBytes) return TGEMM_ERR_WORKSPACE_LIMIT;
+    return scratch_address(&w->ptr);
+  }
   hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
   if (s != nullptr && hipStreamIsCapturing(s, &cs) == hipSuccess &&
       cs != hipStreamCaptureStatusNone) {
@@ -406,6 +448,19 @@ extern "C" int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t
   return run_impl(kWsCached, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
                   out_loss, out_grad, reinterpret_cast<hipStream_t>(stream));
 }
+
+extern "C" int tgemm_run_noalloc(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                 const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
+                                 int64_t ldc, int epilogue, const int32_t* labels,
+                                 float* out_loss, void* out_grad, void* stream) {
+  const int st = tgemm_validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
+                                out_loss, out_grad);
+  if (st != TGEMM_OK) return st;
+  return run_impl(kWsScratch, transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue, labels,
+                  out_loss, out_grad, reinterpret_cast<hipStream_t>(stream));
+}
+
+extern "C" int64_t tgemm_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
 
 // fp8 (e4m3fn) operands.  No K split, no matrix-vector or K = 1 shortcut:
 // every element goes through the cast.  Two routes with the same bits:

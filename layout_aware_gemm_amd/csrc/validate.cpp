@@ -76,6 +76,7 @@ extern "C" const char* tgemm_status_string(int status) {
     case TGEMM_ERR_UNSUPPORTED: return "TGEMM_ERR_UNSUPPORTED";
     case TGEMM_ERR_HIP: return "TGEMM_ERR_HIP";
     case TGEMM_ERR_NO_MEMORY: return "TGEMM_ERR_NO_MEMORY";
+    case TGEMM_ERR_WORKSPACE_LIMIT: return "TGEMM_ERR_WORKSPACE_LIMIT";
     default: return "TGEMM_ERR_UNKNOWN";
   }
 }

@@ -22,6 +22,7 @@ TGEMM_ERR_INVALID_ARG = -1
 TGEMM_ERR_UNSUPPORTED = -2
 TGEMM_ERR_HIP = -3
 TGEMM_ERR_NO_MEMORY = -4
+TGEMM_ERR_WORKSPACE_LIMIT = -5
 
 EPI_STORE_BF16 = 0
 EPI_STORE_F32 = 1
@@ -32,7 +33,7 @@ EPI_ROPE_COSSIN = 4
 EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
            "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k",
            "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version",
-           "tgemm_release_workspace")
+           "tgemm_release_workspace", "tgemm_run_noalloc", "tgemm_noalloc_scratch_bytes")
 
 
 class TgemmError(RuntimeError):
@@ -81,6 +82,10 @@ def lib():
         L.tgemm_version.restype = ctypes.c_int
         L.tgemm_release_workspace.argtypes = [vp]
         L.tgemm_release_workspace.restype = ctypes.c_int
+        L.tgemm_run_noalloc.argtypes = L.tgemm_run.argtypes
+        L.tgemm_run_noalloc.restype = ctypes.c_int
+        L.tgemm_noalloc_scratch_bytes.argtypes = []
+        L.tgemm_noalloc_scratch_bytes.restype = ctypes.c_int64
         _lib = L
     return _lib
 
@@ -120,6 +125,24 @@ def run(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue,
     if check and st != TGEMM_OK:
         raise TgemmError(st)
     return st
+
+
+def run_noalloc(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue,
+                labels=None, out_loss=None, out_grad=None, stream=None, check=True):
+    """Call ``tgemm_run_noalloc``: as ``run``, with every scratch buffer in
+    the library's fixed per-device array (no device allocation)."""
+    dev = A.device if isinstance(A, torch.Tensor) and A.is_cuda else None
+    st = lib().tgemm_run_noalloc(_flag(transA), _flag(transB), int(M), int(N), int(K), _ptr(A),
+                                 int(lda), _ptr(B), int(ldb), _ptr(C), int(ldc), int(epilogue),
+                                 _ptr(labels), _ptr(out_loss), _ptr(out_grad),
+                                 _stream(stream, dev))
+    if check and st != TGEMM_OK:
+        raise TgemmError(st, "tgemm_run_noalloc")
+    return st
+
+
+def noalloc_scratch_bytes():
+    return int(lib().tgemm_noalloc_scratch_bytes())
 
 
 def validate(transA, transB, M, N, K, A, lda, B, ldb, C, ldc, epilogue,

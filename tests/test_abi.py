@@ -41,6 +41,7 @@ def test_status_strings():
     assert tgemm.status_string(UNS) == "TGEMM_ERR_UNSUPPORTED"
     assert tgemm.status_string(tgemm.TGEMM_ERR_HIP) == "TGEMM_ERR_HIP"
     assert tgemm.status_string(tgemm.TGEMM_ERR_NO_MEMORY) == "TGEMM_ERR_NO_MEMORY"
+    assert tgemm.status_string(tgemm.TGEMM_ERR_WORKSPACE_LIMIT) == "TGEMM_ERR_WORKSPACE_LIMIT"
     assert tgemm.status_string(-99) == "TGEMM_ERR_UNKNOWN"
 
 
