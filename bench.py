@@ -232,7 +232,9 @@ def fused_ce(steps, warmup):
 
 def rope_tables(steps, warmup):
     """The K=1 RoPE table (cos and sin, bf16 [P, 128]) for 4096 positions
-    and for 256 x 4096 positions: time, GB/s, fraction of HBM peak."""
+    and for 256 x 4096 positions, and the whole RoPE region (tables plus the
+    query's widened head-major copy) at 4096 positions x 32 heads x 128:
+    time, GB/s, fraction of HBM peak."""
     import torch
 
     import workloads
@@ -273,6 +275,23 @@ def rope_tables(steps, warmup):
                                                     torch.equal(sin, ref_s))
             del g
         del pos, inv, cos, sin
+    # the whole region of the listing in one launch: the tables plus the
+    # query [4096, 32*128] widened and permuted to fp32 [32, 4096, 128]
+    rr = workloads.rope_region()
+    q, pos, inv = rr["q"].to(dev), rr["pos"].to(dev), rr["inv_freq"].to(dev)
+    P, HD = rr["q"].shape
+    H = rr["heads"]
+    D = HD // H
+    q_out = torch.empty(H, P, D, dtype=torch.float32, device=dev)
+    cos = torch.empty(P, D, dtype=torch.bfloat16, device=dev)
+    sin = torch.empty_like(cos)
+    msq = time_stream(lambda i: tgemm.run_rope_region(q, HD, P, H, D, pos, 1, inv, cos, sin, D,
+                                                      q_out), steps, warmup, 1)
+    byts = P * HD * 2 + P * HD * 4 + 2 * P * D * 2 + P * 8 + (D // 2) * 4
+    out["rope_region_4096x32x128_us"] = round(msq * 1e3, 2)
+    out["rope_region_4096x32x128_GBps"] = round(byts / (msq * 1e-3) / 1e9, 1)
+    out["rope_region_4096x32x128_frac_of_hbm"] = round(byts / (msq * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    del q, pos, inv, q_out, cos, sin
     return out
 
 

@@ -239,6 +239,44 @@ TGEMM_API int tgemm_validate_fp8(char transA, char transB, int64_t M, int64_t N,
                   const void* A, int64_t lda, const void* B, int64_t ldb,
                   const void* C, int64_t ldc, int epilogue, const float* scales);
 
+/*
+ * The RoPE region of "Schedule a small matmul op as a reduction (or
+ * pointwise) op" as far as that page's %kernel_math listing goes, in one
+ * launch (the page's closing remark: the section fused into a single
+ * kernel, the K = 1 matmul included):
+ *   - the cos / sin tables of the positions, exactly as tgemm_run with
+ *     TGEMM_EPI_ROPE_COSSIN and K = 1: t = fp32(pos[p]) * inv_freq[i]
+ *     (i < F = D/2), cos_out / sin_out[p, i] and [p, i + F] = bf16(cos t) /
+ *     bf16(sin t) (the listing's T19 .. T26 and the second table output);
+ *   - the query of the listing's first three steps: q [P, ldq] bf16, row p
+ *     holding H heads of D values (head h at columns h*D .. h*D + D-1),
+ *     viewed as [P, H, D] (T5), permuted to [H, P, D] (T6) and widened to
+ *     fp32 (T34), written to q_out[(h*P + p)*D + d] (fp32, contiguous
+ *     [H][P][D]).
+ * The rotation that turns these into the region's rotated outputs is not
+ * on the page and is not applied.
+ *
+ *   q, ldq        bf16 query rows, ldq >= H*D (elements).
+ *   P, H, D       positions, heads, head width; P, H >= 1, D >= 2 even.
+ *   pos, spos     int64 positions, element stride spos >= 1.
+ *   inv_freq      fp32 [D/2], contiguous.
+ *   cos_out, sin_out  bf16 [P, ldc], ldc >= D.
+ *   q_out         fp32 [H*P*D].
+ * All pointers are device pointers owned by the caller; outputs must not
+ * alias inputs.  Validation, errors, asynchrony and streams as for
+ * tgemm_run; no workspace.  Returns TGEMM_OK or a negative tgemm_status.
+ */
+TGEMM_API int tgemm_rope_region(const void* q, int64_t ldq, int64_t P, int64_t H, int64_t D,
+                                const int64_t* pos, int64_t spos, const float* inv_freq,
+                                void* cos_out, void* sin_out, int64_t ldc, float* q_out,
+                                void* stream);
+
+/* Host-only argument check of tgemm_rope_region (no GPU access). */
+TGEMM_API int tgemm_validate_rope_region(const void* q, int64_t ldq, int64_t P, int64_t H,
+                                         int64_t D, const int64_t* pos, int64_t spos,
+                                         const float* inv_freq, const void* cos_out,
+                                         const void* sin_out, int64_t ldc, const float* q_out);
+
 /* Human-readable name of a status code (static string, never NULL). */
 TGEMM_API const char* tgemm_status_string(int status);
 

@@ -462,6 +462,23 @@ extern "C" int tgemm_run_noalloc(char transA, char transB, int64_t M, int64_t N,
 
 extern "C" int64_t tgemm_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
 
+extern "C" int tgemm_rope_region(const void* q, int64_t ldq, int64_t P, int64_t H, int64_t D,
+                                 const int64_t* pos, int64_t spos, const float* inv_freq,
+                                 void* cos_out, void* sin_out, int64_t ldc, float* q_out,
+                                 void* stream) {
+  const int st = tgemm_validate_rope_region(q, ldq, P, H, D, pos, spos, inv_freq, cos_out,
+                                            sin_out, ldc, q_out);
+  if (st != TGEMM_OK) return st;
+  if (verbose())
+    fprintf(stderr, "tgemm: rope region P=%lld H=%lld D=%lld\n", (long long)P, (long long)H,
+            (long long)D);
+  const hipError_t e = launch_rope_region(static_cast<const uint16_t*>(q), ldq, P, H, D, pos, spos,
+                                          inv_freq, static_cast<uint16_t*>(cos_out),
+                                          static_cast<uint16_t*>(sin_out), ldc, q_out,
+                                          reinterpret_cast<hipStream_t>(stream));
+  return e == hipErrorInvalidValue ? TGEMM_ERR_UNSUPPORTED : status_of(e);
+}
+
 // fp8 (e4m3fn) operands.  No K split, no matrix-vector or K = 1 shortcut:
 // every element goes through the cast.  Two routes with the same bits:
 //  - cast on load, on the GEMM kernel's register path (the direct copies

@@ -74,17 +74,17 @@ __device__ __forceinline__ void sincos_t(float t, float& sn, float& cs) {
 // thread takes RPT rows that are `slots` rows apart.
 constexpr int kRopeRows = 2;
 
-// One thread per (row slot, group of 8 columns).
+// One thread per (row slot, group of 8 columns); `gid` is the thread's index
+// in the table's part of the grid.
 template <int RPT>
-__global__ void __launch_bounds__(256) k1_rope_kernel(
-    const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf, int64_t sinv,
-    int M, int N, uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out, int64_t ldc,
-    int vec_ok, uint32_t spb) {
+__device__ __forceinline__ void rope_table_part(
+    uint32_t gid, const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf,
+    int64_t sinv, int M, int N, uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out,
+    int64_t ldc, int vec_ok, uint32_t spb) {
   // (the grid has fewer than 2^32 threads, so 32-bit index arithmetic)
   const uint32_t groups = (uint32_t)(N + 7) >> 3;
   const uint32_t slots = spb ? ((uint32_t)M + spb * RPT - 1) / (spb * RPT) * spb
                             : ((uint32_t)M + RPT - 1) / RPT;
-  const uint32_t gid = blockIdx.x * blockDim.x + threadIdx.x;
   const uint32_t rs = gid / groups;
   if (rs >= slots) return;
   const int c0 = (int)(gid - rs * groups) * 8;
@@ -154,6 +154,67 @@ __global__ void __launch_bounds__(256) k1_rope_kernel(
         so[c + N] = sb;
       }
     }
+  }
+}
+
+template <int RPT>
+__global__ void __launch_bounds__(256) k1_rope_kernel(
+    const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf, int64_t sinv,
+    int M, int N, uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out, int64_t ldc,
+    int vec_ok, uint32_t spb) {
+  rope_table_part<RPT>(blockIdx.x * blockDim.x + threadIdx.x, pos, spos, invf, sinv, M, N,
+                       cos_out, sin_out, ldc, vec_ok, spb);
+}
+
+// The query part of the RoPE region ("Schedule a small matmul op as a
+// reduction (or pointwise) op", the %kernel_math listing: the [P, H*D] bf16
+// query viewed as [P, H, D], permuted to [H, P, D] and cast to fp32).  One
+// thread per 8 consecutive elements of a query row: a 16-byte load, the
+// exact bf16 -> fp32 widening, and two 16-byte streaming stores into the
+// head-major fp32 output.  The 64 lanes of a wave read 1 KB of one query row
+// and write it as 512-byte runs of the output rows of consecutive heads.
+__device__ __forceinline__ void rope_query_part(uint64_t g, const uint16_t* __restrict__ q,
+                                                int64_t ldq, int64_t P, int64_t H, int64_t D,
+                                                float* __restrict__ out, int vec_ok) {
+  const int64_t per_row = (H * D + 7) >> 3;
+  const int64_t p = (int64_t)(g / (uint64_t)per_row);
+  if (p >= P) return;
+  const int64_t c0 = (int64_t)(g - (uint64_t)p * per_row) * 8;
+  const uint16_t* src = q + p * ldq + c0;
+  if (vec_ok && c0 + 8 <= H * D) {
+    // D % 8 == 0: the 8 elements belong to one head
+    const int64_t h = c0 / D, d = c0 - h * D;
+    const uint4 v = *reinterpret_cast<const uint4*>(src);
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const f32x4v lo = {from_bf16(v.x & 0xffffu), from_bf16(v.x >> 16), from_bf16(v.y & 0xffffu),
+                       from_bf16(v.y >> 16)};
+    const f32x4v hi = {from_bf16(v.z & 0xffffu), from_bf16(v.z >> 16), from_bf16(v.w & 0xffffu),
+                       from_bf16(v.w >> 16)};
+    float* dst = out + (h * P + p) * D + d;
+    __builtin_nontemporal_store(lo, reinterpret_cast<f32x4v*>(dst));
+    __builtin_nontemporal_store(hi, reinterpret_cast<f32x4v*>(dst + 4));
+  } else {
+    for (int e = 0; e < 8 && c0 + e < H * D; ++e) {
+      const int64_t c = c0 + e, h = c / D, d = c - h * D;
+      out[(h * P + p) * D + d] = from_bf16(src[e]);
+    }
+  }
+}
+
+// The region in one launch: workgroups [0, tbl_blocks) build the cos / sin
+// tables of the positions (the K = 1 product and its epilogue), the rest
+// widen and permute the query.  The two parts share no data.
+__global__ void __launch_bounds__(256) rope_region_kernel(
+    const int64_t* __restrict__ pos, int64_t spos, const float* __restrict__ invf, int P, int F,
+    uint16_t* __restrict__ cos_out, uint16_t* __restrict__ sin_out, int64_t ldc, int vec_tbl,
+    uint32_t spb, uint32_t tbl_blocks, const uint16_t* __restrict__ q, int64_t ldq, int64_t H,
+    int64_t D, float* __restrict__ q_out, int vec_q) {
+  if (blockIdx.x < tbl_blocks) {
+    rope_table_part<kRopeRows>(blockIdx.x * blockDim.x + threadIdx.x, pos, spos, invf, 1, P, F,
+                               cos_out, sin_out, ldc, vec_tbl, spb);
+  } else {
+    const uint64_t g = (uint64_t)(blockIdx.x - tbl_blocks) * blockDim.x + threadIdx.x;
+    rope_query_part(g, q, ldq, P, H, D, q_out, vec_q);
   }
 }
 
@@ -253,21 +314,52 @@ inline unsigned grid_for(int64_t threads) { return (unsigned)((threads + 255) / 
 
 }  // namespace
 
+struct RopeGeom {
+  int vec_ok;
+  uint32_t spb;
+  int64_t threads;
+};
+
+static RopeGeom rope_geom(const float* invf, int64_t sinv, int M, int N, const uint16_t* cos_out,
+                   const uint16_t* sin_out, int64_t ldc) {
+  RopeGeom g;
+  g.vec_ok = sinv == 1 && (reinterpret_cast<uintptr_t>(invf) & 15) == 0 &&
+             (reinterpret_cast<uintptr_t>(cos_out) & 15) == 0 &&
+             (reinterpret_cast<uintptr_t>(sin_out) & 15) == 0 && ldc % 8 == 0 && N % 8 == 0;
+  const int64_t groups = (N + 7) / 8;
+  g.spb = groups <= 256 && 256 % groups == 0 ? (uint32_t)(256 / groups) : 0;
+  const int64_t slots = g.spb ? ((int64_t)M + g.spb * kRopeRows - 1) / (g.spb * kRopeRows) * g.spb
+                              : ((int64_t)M + kRopeRows - 1) / kRopeRows;
+  g.threads = slots * groups;
+  return g;
+}
+
 hipError_t launch_k1_rope(const int64_t* pos, int64_t spos, const float* invf, int64_t sinv,
                           int M, int N, uint16_t* cos_out, uint16_t* sin_out, int64_t ldc,
                           hipStream_t s) {
-  const int vec_ok = sinv == 1 && (reinterpret_cast<uintptr_t>(invf) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(cos_out) & 15) == 0 &&
-                     (reinterpret_cast<uintptr_t>(sin_out) & 15) == 0 && ldc % 8 == 0 &&
-                     N % 8 == 0;
-  const int64_t groups = (N + 7) / 8;
-  const uint32_t spb = groups <= 256 && 256 % groups == 0 ? (uint32_t)(256 / groups) : 0;
-  const int64_t slots = spb ? ((int64_t)M + spb * kRopeRows - 1) / (spb * kRopeRows) * spb
-                            : ((int64_t)M + kRopeRows - 1) / kRopeRows;
-  const int64_t threads = slots * groups;
-  if (threads >= (int64_t(1) << 32)) return hipErrorInvalidValue;  // 32-bit thread index
-  hipLaunchKernelGGL(k1_rope_kernel<kRopeRows>, dim3(grid_for(threads)), dim3(256), 0, s, pos,
-                     spos, invf, sinv, M, N, cos_out, sin_out, ldc, vec_ok, spb);
+  const RopeGeom g = rope_geom(invf, sinv, M, N, cos_out, sin_out, ldc);
+  if (g.threads >= (int64_t(1) << 32)) return hipErrorInvalidValue;  // 32-bit thread index
+  hipLaunchKernelGGL(k1_rope_kernel<kRopeRows>, dim3(grid_for(g.threads)), dim3(256), 0, s, pos,
+                     spos, invf, sinv, M, N, cos_out, sin_out, ldc, g.vec_ok, g.spb);
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_region(const uint16_t* q, int64_t ldq, int64_t P, int64_t H, int64_t D,
+                              const int64_t* pos, int64_t spos, const float* invf,
+                              uint16_t* cos_out, uint16_t* sin_out, int64_t ldc, float* q_out,
+                              hipStream_t s) {
+  const int F = (int)(D / 2);
+  const RopeGeom g = rope_geom(invf, 1, (int)P, F, cos_out, sin_out, ldc);
+  const int64_t tbl_blocks = (g.threads + 255) / 256;
+  const int64_t q_threads = P * ((H * D + 7) / 8);
+  const int64_t q_blocks = (q_threads + 255) / 256;
+  if (g.threads >= (int64_t(1) << 32) || tbl_blocks + q_blocks >= (int64_t(1) << 31))
+    return hipErrorInvalidValue;
+  const int vec_q = (reinterpret_cast<uintptr_t>(q) & 15) == 0 && ldq % 8 == 0 && D % 8 == 0 &&
+                    (reinterpret_cast<uintptr_t>(q_out) & 15) == 0;
+  hipLaunchKernelGGL(rope_region_kernel, dim3((unsigned)(tbl_blocks + q_blocks)), dim3(256), 0, s,
+                     pos, spos, invf, (int)P, F, cos_out, sin_out, ldc, g.vec_ok, g.spb,
+                     (uint32_t)tbl_blocks, q, ldq, H, D, q_out, vec_q);
   return hipGetLastError();
 }
 

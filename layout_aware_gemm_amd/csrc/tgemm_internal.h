@@ -94,6 +94,14 @@ hipError_t launch_k1_outer_f32(const float* a, int64_t sa, const float* b, int64
                                int N, float* C, int64_t ldc, hipStream_t s);
 hipError_t launch_k1_outer_bf16(const uint16_t* a, int64_t sa, const uint16_t* b, int64_t sb,
                                 int M, int N, void* C, int64_t ldc, bool out_f32, hipStream_t s);
+// The RoPE region in one launch: the cos / sin tables (D = 2F columns, F
+// = D/2 inverse frequencies, contiguous) of P positions, and the query q
+// [P, ldq] bf16 (H heads of D) widened and permuted into q_out fp32
+// [H][P][D] (defined in k1.hip).
+hipError_t launch_rope_region(const uint16_t* q, int64_t ldq, int64_t P, int64_t H, int64_t D,
+                              const int64_t* pos, int64_t spos, const float* invf,
+                              uint16_t* cos_out, uint16_t* sin_out, int64_t ldc, float* q_out,
+                              hipStream_t s);
 // Cross-entropy of the K = 1 logits y[m, n] = a[m] * b[n] (bf16 operands):
 // loss[m] = logsumexp_n y - y[m, labels[m]]; grad (optional, row stride ldg)
 // = bf16(softmax - onehot).  One workgroup per row.

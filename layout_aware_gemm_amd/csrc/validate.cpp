@@ -69,6 +69,23 @@ extern "C" int tgemm_validate_fp8(char transA, char transB, int64_t M, int64_t N
                         nullptr, nullptr);
 }
 
+extern "C" int tgemm_validate_rope_region(const void* q, int64_t ldq, int64_t P, int64_t H,
+                                          int64_t D, const int64_t* pos, int64_t spos,
+                                          const float* inv_freq, const void* cos_out,
+                                          const void* sin_out, int64_t ldc, const float* q_out) {
+  if (P < 1 || H < 1 || D < 2 || (D & 1) != 0) return TGEMM_ERR_INVALID_ARG;
+  if (P > kMaxDim || H > kMaxDim || D > kMaxDim) return TGEMM_ERR_UNSUPPORTED;
+  if (q == nullptr || pos == nullptr || inv_freq == nullptr || cos_out == nullptr ||
+      sin_out == nullptr || q_out == nullptr)
+    return TGEMM_ERR_INVALID_ARG;
+  if (spos < 1 || ldc < D) return TGEMM_ERR_INVALID_ARG;
+  if (H > INT64_MAX / D || ldq < H * D) return TGEMM_ERR_INVALID_ARG;
+  if (ldq > INT64_MAX / P || ldc > INT64_MAX / P || spos > INT64_MAX / P ||
+      H * D > INT64_MAX / P / 4)
+    return TGEMM_ERR_UNSUPPORTED;
+  return TGEMM_OK;
+}
+
 extern "C" const char* tgemm_status_string(int status) {
   switch (status) {
     case TGEMM_OK: return "TGEMM_OK";

@@ -33,7 +33,8 @@ EPI_ROPE_COSSIN = 4
 EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
            "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k",
            "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version",
-           "tgemm_release_workspace", "tgemm_run_noalloc", "tgemm_noalloc_scratch_bytes")
+           "tgemm_release_workspace", "tgemm_run_noalloc", "tgemm_noalloc_scratch_bytes",
+           "tgemm_rope_region", "tgemm_validate_rope_region")
 
 
 class TgemmError(RuntimeError):
@@ -86,6 +87,11 @@ def lib():
         L.tgemm_run_noalloc.restype = ctypes.c_int
         L.tgemm_noalloc_scratch_bytes.argtypes = []
         L.tgemm_noalloc_scratch_bytes.restype = ctypes.c_int64
+        L.tgemm_rope_region.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]
+        L.tgemm_rope_region.restype = ctypes.c_int
+        L.tgemm_validate_rope_region.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64,
+                                                 vp]
+        L.tgemm_validate_rope_region.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -367,6 +373,48 @@ def rope_cos_sin(pos, inv_freq, stream=None):
     run("N", tb, P, F, 1, pos, pos.stride(0), inv_freq, ldb, cos, 2 * F, EPI_ROPE_COSSIN,
         out_grad=sin, stream=stream)
     return cos, sin
+
+
+def run_rope_region(q, ldq, P, H, D, pos, spos, inv_freq, cos, sin, ldc, q_out, stream=None,
+                    check=True):
+    """Call ``tgemm_rope_region`` (pointers may be tensors or addresses)."""
+    dev = q.device if isinstance(q, torch.Tensor) and q.is_cuda else None
+    st = lib().tgemm_rope_region(_ptr(q), int(ldq), int(P), int(H), int(D), _ptr(pos), int(spos),
+                                 _ptr(inv_freq), _ptr(cos), _ptr(sin), int(ldc), _ptr(q_out),
+                                 _stream(stream, dev))
+    if check and st != TGEMM_OK:
+        raise TgemmError(st, "tgemm_rope_region")
+    return st
+
+
+def validate_rope_region(q, ldq, P, H, D, pos, spos, inv_freq, cos, sin, ldc, q_out):
+    """Host-only ``tgemm_validate_rope_region``."""
+    return lib().tgemm_validate_rope_region(_ptr(q), int(ldq), int(P), int(H), int(D), _ptr(pos),
+                                            int(spos), _ptr(inv_freq), _ptr(cos), _ptr(sin),
+                                            int(ldc), _ptr(q_out))
+
+
+def rope_region(q, pos, inv_freq, heads, stream=None):
+    """The RoPE region in one launch: q bf16 [P, heads*D] (row-major, any
+    row stride), pos int64 [P], inv_freq fp32 [D/2].  Returns (q_heads fp32
+    [heads, P, D], cos bf16 [P, D], sin bf16 [P, D])."""
+    if q.dtype != torch.bfloat16 or pos.dtype != torch.int64 or inv_freq.dtype != torch.float32:
+        raise TypeError("q must be bf16, pos int64, inv_freq fp32")
+    if q.dim() != 2 or q.stride(1) != 1 or pos.dim() != 1 or inv_freq.dim() != 1:
+        raise ValueError("q must be a row-major [P, H*D] matrix, pos and inv_freq 1-D")
+    if not inv_freq.is_contiguous():
+        raise ValueError("inv_freq must be contiguous")
+    _check_dev(q, pos, inv_freq)
+    P, HD = q.shape
+    D = 2 * inv_freq.shape[0]
+    if pos.shape[0] != P or HD != heads * D:
+        raise ValueError("shapes of q, pos, inv_freq and heads do not agree")
+    q_out = torch.empty(heads, P, D, dtype=torch.float32, device=q.device)
+    cos = torch.empty(P, D, dtype=torch.bfloat16, device=q.device)
+    sin = torch.empty(P, D, dtype=torch.bfloat16, device=q.device)
+    run_rope_region(q, q.stride(0), P, heads, D, pos, pos.stride(0), inv_freq, cos, sin, D, q_out,
+                    stream=stream)
+    return q_out, cos, sin
 
 
 def outer_f32(a, b, stream=None):

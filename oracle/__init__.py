@@ -17,11 +17,12 @@ Everything is computed from the plain definitions in fp64 with NumPy:
                      matmul epilogues" (the attempted fusion: max, shifted
                      exp, sum, log, loss, softmax minus one-hot) and the
                      tile-wise combine its question-and-answer part describes.
-* ``k1_outer`` / ``rope_angles`` / ``rope_tables``
-                  -- the K=1 matmul as one elementwise multiply and the cos /
-                     sin tables of its angles, repeated along the last axis
-                     ("Schedule a small matmul op as a reduction (or
-                     pointwise) op": the %kernel_math listing and the
+* ``k1_outer`` / ``rope_angles`` / ``rope_tables`` / ``rope_region``
+                  -- the K=1 matmul as one elementwise multiply, the cos /
+                     sin tables of its angles, repeated along the last axis,
+                     and the query's view / permute / widening steps of the
+                     same region ("Schedule a small matmul op as a reduction
+                     (or pointwise) op": the %kernel_math listing and the
                      proposed decomposition).
 * ``bf16``        -- exact bf16 decode and single-rounding round-to-nearest-
                      even encode.
@@ -40,7 +41,7 @@ tolerance, because accumulation order on the GPU differs from BLAS's.
 from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
 from .gemm import op_matrix, gemm
 from .xent import cross_entropy, logsumexp_rows, tile_partials, merge_partials, merge_pair
-from .rope import k1_outer, rope_angles, rope_tables
+from .rope import k1_outer, rope_angles, rope_tables, rope_region
 from .fp8 import E4M3_MAX, e4m3_round, quantize, gemm_fp8
 
 __all__ = [
@@ -56,6 +57,7 @@ __all__ = [
     "k1_outer",
     "rope_angles",
     "rope_tables",
+    "rope_region",
     "E4M3_MAX",
     "e4m3_round",
     "quantize",

@@ -25,7 +25,7 @@ frequencies] product here has the same bits (a pin checks this).
 
 import numpy as np
 
-from .bf16 import f64_to_bf16_bits
+from .bf16 import bf16_bits_to_f64, f64_to_bf16_bits
 
 
 def k1_outer(a_f32, b_f32):
@@ -55,3 +55,25 @@ def rope_tables(pos_i64, inv_freq_f32):
     angles = rope_angles(pos_i64, inv_freq_f32)
     wide = np.hstack([angles, angles]).astype(np.float64)
     return angles, f64_to_bf16_bits(np.cos(wide)), f64_to_bf16_bits(np.sin(wide))
+
+
+def rope_region(q_bits, ldq, P, H, D, pos_i64, inv_freq_f32):
+    """The region's query steps and tables, as far as the listing goes.
+
+    The query rows (bf16 bits, P rows of stride ldq, H heads of D values per
+    row) are viewed as [P, H, D], permuted to [H, P, D] and widened from bf16
+    (exact); the tables are ``rope_tables`` of the positions with the D/2
+    inverse frequencies.  Returns (q_heads fp64 [H, P, D], angles, cos bits,
+    sin bits).  The rotation that would combine them is not on the page.
+    """
+    flat = np.asarray(q_bits).reshape(-1)
+    if flat.size < (P - 1) * ldq + H * D or ldq < H * D:
+        raise ValueError("query buffer too small for its shape and row stride")
+    rows = np.stack([flat[p * ldq: p * ldq + H * D] for p in range(P)])     # [P, H*D]
+    as_heads = rows.reshape(P, H, D)                                         # view
+    head_major = np.ascontiguousarray(as_heads.transpose(1, 0, 2))          # permute
+    q_heads = bf16_bits_to_f64(head_major)                                   # widen
+    angles, cos_bits, sin_bits = rope_tables(pos_i64, inv_freq_f32)
+    if cos_bits.shape[1] != D:
+        raise ValueError("the tables are D = 2 * len(inv_freq) wide")
+    return q_heads, angles, cos_bits, sin_bits

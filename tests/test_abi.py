@@ -158,3 +158,18 @@ def test_set_fp8_cast_once_roundtrip():
     assert tgemm.set_fp8_cast_once(prev) == 0
     with pytest.raises(tgemm.TgemmError):
         tgemm.set_fp8_cast_once(2)
+
+
+def test_rope_region_validation():
+    P_ = 64  # any non-null address: validation never dereferences
+    v = tgemm.validate_rope_region
+    assert v(P_, 4096, 4096, 32, 128, P_, 1, P_, P_, P_, 128, P_) == OK
+    assert v(P_, 4095, 4096, 32, 128, P_, 1, P_, P_, P_, 128, P_) == INV   # ldq < H*D
+    assert v(P_, 4096, 4096, 32, 127, P_, 1, P_, P_, P_, 128, P_) == INV   # odd D
+    assert v(P_, 4096, 0, 32, 128, P_, 1, P_, P_, P_, 128, P_) == INV      # no positions
+    assert v(P_, 4096, 4096, 32, 128, P_, 1, P_, P_, P_, 127, P_) == INV   # ldc < D
+    assert v(P_, 4096, 4096, 32, 128, P_, 0, P_, P_, P_, 128, P_) == INV   # position stride
+    assert v(None, 4096, 4096, 32, 128, P_, 1, P_, P_, P_, 128, P_) == INV
+    assert v(P_, 4096, 4096, 32, 128, P_, 1, P_, P_, P_, 128, None) == INV
+    with pytest.raises(tgemm.TgemmError):
+        tgemm.run_rope_region(P_, 4096, 4096, 32, 127, P_, 1, P_, P_, P_, 128, P_, stream=0)

@@ -109,3 +109,52 @@ def test_outer_f32_random_exact():
     c = tgemm.outer_f32(torch.from_numpy(a).to(dev()), torch.from_numpy(b).to(dev()))
     torch.cuda.synchronize()
     assert np.array_equal(c.cpu().numpy(), oracle.k1_outer(a, b))
+
+
+def test_rope_region_page_size():
+    """The region at the listing's sizes in one launch: the query
+    [4096, 32*128] widened and permuted to fp32 [32, 4096, 128] must equal
+    the oracle bit for bit (a bf16 -> fp32 widening is exact), and the
+    tables must match the oracle as the K = 1 path's do."""
+    w = workloads.rope_region()
+    q, pos, inv = w["q"].to(dev()), w["pos"].to(dev()), w["inv_freq"].to(dev())
+    H = w["heads"]
+    q_heads, cos, sin = tgemm.rope_region(q, pos, inv, H)
+    torch.cuda.synchronize()
+    P, HD = w["q"].shape
+    D = HD // H
+    ref_q, _, rc, rs = oracle.rope_region(bits(w["q"]).reshape(-1), HD, P, H, D,
+                                          w["pos"].numpy(), w["inv_freq"].numpy())
+    assert q_heads.shape == (H, P, D)
+    assert np.array_equal(q_heads.cpu().numpy().astype(np.float64), ref_q)
+    fc, fs = check_tables(cos, sin, w["pos"], w["inv_freq"])
+    assert fc > 0.99 and fs > 0.99
+    # the same tables as the K = 1 entry point, bit for bit
+    c1, s1 = tgemm.rope_cos_sin(pos, inv)
+    torch.cuda.synchronize()
+    assert torch.equal(c1, cos) and torch.equal(s1, sin)
+
+
+@pytest.mark.parametrize("P,H,D,qpad,cpad,spos", [(1, 1, 2, 0, 0, 1), (37, 3, 10, 3, 1, 2),
+                                                  (333, 5, 16, 0, 8, 1), (70, 2, 128, 5, 0, 3)])
+def test_rope_region_ragged_and_strided(P, H, D, qpad, cpad, spos):
+    """Odd head widths (the scalar path), padded query rows and table rows,
+    strided positions; nothing is written past each table row's D columns."""
+    g = torch.Generator().manual_seed(P * H + D)
+    ldq = H * D + qpad
+    q = torch.randn(P, ldq, generator=g).to(torch.bfloat16)
+    pos = torch.randint(-3000, 3000, (P * spos,), generator=g, dtype=torch.int64)
+    inv = workloads.inv_freq(D)
+    ldc = D + cpad
+    cos = torch.full((P, ldc), float("nan"), dtype=torch.bfloat16, device=dev())
+    sin = torch.full((P, ldc), float("nan"), dtype=torch.bfloat16, device=dev())
+    q_out = torch.full((H * P * D,), float("nan"), dtype=torch.float32, device=dev())
+    tgemm.run_rope_region(q.to(dev()), ldq, P, H, D, pos.to(dev()), spos, inv.to(dev()), cos, sin,
+                          ldc, q_out)
+    torch.cuda.synchronize()
+    ref_q, _, rc, rs = oracle.rope_region(bits(q).reshape(-1), ldq, P, H, D,
+                                          pos.numpy()[::spos], inv.numpy())
+    assert np.array_equal(q_out.cpu().numpy().reshape(H, P, D).astype(np.float64), ref_q)
+    check_tables(cos[:, :D], sin[:, :D], pos[::spos], inv)
+    if cpad:
+        assert torch.isnan(cos[:, D:].float()).all() and torch.isnan(sin[:, D:].float()).all()

@@ -329,6 +329,38 @@ def test_rope_inv_freq_input():
         assert inv[i] == np.float32(10000.0 ** (-(2 * i) / 128.0))
 
 
+def test_rope_region_query_steps_brute_force():
+    """View [P, H, D], permute to [H, P, D], widen: element by element with
+    Python loops and the struct decode, on a strided tiny case."""
+    rng = np.random.default_rng(9)
+    P, H, D, ldq = 5, 3, 4, 14
+    bits = rng.integers(0, 2 ** 16, size=(P - 1) * ldq + H * D).astype(np.uint16)
+    bits[(bits & 0x7F80) == 0x7F80] = 0x3F80          # no NaN / inf patterns
+    pos = np.array([0, 3, 7, 100, 4095])
+    q_heads, ang, cos, sin = oracle.rope_region(bits, ldq, P, H, D, pos, workloads.inv_freq(D).numpy())
+    assert q_heads.shape == (H, P, D)
+    for h in range(H):
+        for p in range(P):
+            for d in range(D):
+                assert q_heads[h, p, d] == py_bf16_to_float(int(bits[p * ldq + h * D + d]))
+    ang2, cos2, sin2 = oracle.rope_tables(pos, workloads.inv_freq(D).numpy())
+    assert np.array_equal(ang, ang2) and np.array_equal(cos, cos2) and np.array_equal(sin, sin2)
+
+
+def test_rope_region_matches_torch_view_permute():
+    """Library cross-check: torch's view / permute / float of the same bf16
+    tensor, at the page's shapes ([1, 4096, 4096] -> [1, 4096, 32, 128] ->
+    [1, 32, 4096, 128])."""
+    w = workloads.rope_region()
+    q = w["q"]
+    P, HD = q.shape
+    H, D = w["heads"], HD // w["heads"]
+    q_heads, _, _, _ = oracle.rope_region(workloads.bf16_bits(q), HD, P, H, D, w["pos"].numpy(),
+                                          w["inv_freq"].numpy())
+    ref = q.view(1, P, H, D).permute(0, 2, 1, 3).float()
+    assert np.array_equal(q_heads, ref[0].double().numpy())
+
+
 # -------------------------------------------------------------- golden
 def test_golden_page_shapes():
     with open(os.path.join(GOLDEN, "page_shapes.json")) as f:
@@ -350,6 +382,12 @@ def test_golden_page_shapes():
     assert [1, 1] + list(cos.shape) == r["outputs_T29_T31"]["shape"]
     assert [1, 1] + list(sin.shape) == r["outputs_T29_T31"]["shape"]
     assert list(workloads.rope()["inv_freq"].shape) == r["inv_freq_T3"]["shape"]
+    rr = workloads.rope_region()
+    assert [1] + list(rr["q"].shape) == r["query_T0"]["shape"]
+    H = rr["heads"]
+    D = rr["q"].shape[1] // H
+    assert [1, rr["q"].shape[0], H, D] == r["view_T5"]["shape"]
+    assert [1, H, rr["q"].shape[0], D] == r["permute_T6"]["shape"] == r["cast_T34"]["shape"]
 
 
 # --------------------------------------------------------------- fp8 (e4m3fn)

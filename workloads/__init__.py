@@ -23,6 +23,8 @@ Workloads (shapes and distributions of the pages' examples):
                    "Schedule a small matmul op as a reduction (or pointwise)
                    op" (its fusion inputs)                          deterministic
 * ``rope_batched`` the same table for ``batch`` sequences of 0..4095
+* ``rope_region``  the same positions and frequencies with the region's
+                   query bf16[4096, 32*128] N(0,1) (the listing's T0) seed 1006
 * ``fp8_linear``   X bf16[4096,4096] N(0,1), W bf16[3072,4096] N(0,0.02) with
                    the cast scales {10, 1000} -- the float8 linear of "Improve
                    the Inductor generated kernel for the pattern of output1 =
@@ -38,6 +40,7 @@ import numpy as np
 import torch
 
 SEEDS = {"tiny_ce": 1001, "nt_mlp": 1002, "layout_sweep": 1003, "ce_vocab": 1004,
+         "rope_region": 1006,
          "fp8_linear": 1005}
 
 
@@ -115,6 +118,15 @@ def inv_freq(dim=128, base=10000.0):
 
 def rope(seq=4096, dim=128):
     return {"pos": torch.arange(seq, dtype=torch.int64), "inv_freq": inv_freq(dim)}
+
+
+def rope_region(seed=SEEDS["rope_region"], seq=4096, heads=32, dim=128):
+    """The region's inputs: the query bf16 [seq, heads*dim] N(0,1) (the
+    listing's T0, [1, 4096, 4096]), positions 0..seq-1 and the inverse
+    frequencies of ``rope``."""
+    g = _gen(seed)
+    return {"q": randn_bf16((seq, heads * dim), 1.0, g), "heads": heads,
+            "pos": torch.arange(seq, dtype=torch.int64), "inv_freq": inv_freq(dim)}
 
 
 def rope_batched(batch=256, seq=4096, dim=128):
