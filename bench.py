@@ -227,7 +227,7 @@ def fused_ce(steps, warmup):
         "ce_grad_rows_per_s": round(Mc / (ms_ceg * 1e-3), 1),
         "ce_grad_ms": round(ms_ceg, 4),
     }
-    return out, Hs, Wv, g
+    return out, Hs, Wv, g, lab
 
 
 def rope_tables(steps, warmup):
@@ -397,7 +397,7 @@ def main():
     if not args.only_nt:
         # ---- fused cross-entropy GEMM ------------------------------------
         Mc, Nc, Kc = 4096, 32000, 4096
-        ce_out, Hs, Wv, g = fused_ce(max(5, K_ // 5), max(2, W_ // 5))
+        ce_out, Hs, Wv, g, lab_ce = fused_ce(max(5, K_ // 5), max(2, W_ // 5))
         secondary.update(ce_out)
         ce_fl = 2.0 * Mc * Nc * Kc
         # the GEMMs that consume the gradient, operands read as stored:
@@ -410,7 +410,27 @@ def main():
                                                 tgemm.EPI_STORE_BF16), max(5, K_ // 5), 2, 1)
         secondary["ce_bwd_dH_NN_tflops"] = round(ce_fl / (ms_dh * 1e-3) / 1e12, 2)
         secondary["ce_bwd_dW_TN_tflops"] = round(ce_fl / (ms_dw * 1e-3) / 1e12, 2)
-        del Hs, Wv, g, dH, dW
+        # the same backward with the gradient finished on load: the fused CE
+        # without its rescale pass (the gradient's scale table instead), then
+        # dH and dW reading the unscaled gradient
+        nst = max(5, K_ // 5)
+        lossd = torch.empty(Mc, dtype=torch.float32, device=dev)
+        sc = torch.empty((Nc + 63) // 64, Mc, dtype=torch.float32, device=dev)
+        ms_ced = time_stream(lambda i: tgemm.run_ce_deferred("N", "T", Mc, Nc, Kc, Hs[0], Kc, Wv[0],
+                                                             Kc, lab_ce, lossd, g, Nc, sc),
+                             nst, 2, 1)
+        ms_dh2 = time_stream(lambda i: tgemm.run_ce_grad("N", "N", Mc, Kc, Nc, g, Nc, sc, lab_ce,
+                                                         Wv[0], Kc, dH, Kc, tgemm.EPI_STORE_BF16),
+                             nst, 2, 1)
+        ms_dw2 = time_stream(lambda i: tgemm.run_ce_grad("T", "N", Nc, Kc, Mc, g, Nc, sc, lab_ce,
+                                                         Hs[0], Kc, dW, Kc, tgemm.EPI_STORE_BF16),
+                             nst, 2, 1)
+        secondary["ce_bwd_onload_dH_NN_tflops"] = round(ce_fl / (ms_dh2 * 1e-3) / 1e12, 2)
+        secondary["ce_bwd_onload_dW_TN_tflops"] = round(ce_fl / (ms_dw2 * 1e-3) / 1e12, 2)
+        secondary["ce_fwd_bwd_rescale_pass_route_us"] = round(
+            (ce_out["ce_grad_ms"] + ms_dh + ms_dw) * 1e3, 1)
+        secondary["ce_fwd_bwd_on_load_route_us"] = round((ms_ced + ms_dh2 + ms_dw2) * 1e3, 1)
+        del Hs, Wv, g, dH, dW, sc, lossd
 
         # ---- layout sweep 4096^3 ------------------------------------------
         secondary.update(layout_sweep(K_, W_))

@@ -240,6 +240,54 @@ TGEMM_API int tgemm_validate_fp8(char transA, char transB, int64_t M, int64_t N,
                   const void* C, int64_t ldc, int epilogue, const float* scales);
 
 /*
+ * Cross-entropy with the gradient left for the backward GEMMs to finish
+ * ("Allow reductions in matmul epilogues", the edit note: the
+ * softmax-minus-one-hot matrix is kept for the backward pass).
+ *
+ * As tgemm_run with TGEMM_EPI_CE and a gradient buffer (same arguments,
+ * same loss, bit for bit), except that the pass that rescales the gradient
+ * is not run.  Instead:
+ *   out_e      bf16 [M, N] (row stride lde >= N) receives
+ *              e = bf16(exp(y - m_b)), y the fp32 logit and m_b the maximum
+ *              of y over the block of columns the GEMM's tile reduced (64 or
+ *              128 columns);
+ *   out_scale  fp32 [ceil(N/64) * M] receives, for every 64-column chunk c
+ *              of every row m, s[c*M + m] = exp(m_b - lse[m]) of the block
+ *              holding the chunk.
+ * The gradient is then softmax - onehot = bf16(e * s - [n == labels[m]])
+ * (one fused multiply-add, rounded once), which tgemm_run_ce_grad computes
+ * as it loads e, and which equals bit for bit what the rescale pass of
+ * tgemm_run writes.  K must be >= 2 (a K = 1 product takes the pointwise
+ * path, which has no deferred form): TGEMM_ERR_UNSUPPORTED otherwise.
+ * Validation, errors, asynchrony, streams and workspace as for tgemm_run.
+ */
+TGEMM_API int tgemm_run_ce_deferred(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                    const void* A, int64_t lda, const void* B, int64_t ldb,
+                                    const int32_t* labels, float* out_loss, void* out_e,
+                                    int64_t lde, float* out_scale, void* stream);
+
+/*
+ * A GEMM whose operand A is a cross-entropy gradient left by
+ * tgemm_run_ce_deferred, finished as it is loaded:
+ *   C = op(G) . op(B),  G[t][v] = bf16(e[t*lde + v] * scale[(v/64)*T + t]
+ *                                      - [v == labels[t]])
+ * with G a [T, V] matrix (T token rows, V vocabulary columns) stored as e:
+ * transA 'N' reads it as op(A) = G (T = M, V = K; the gradient of the
+ * hidden states, dH = G . W), 'T' as op(A) = G^T (T = K, V = M; the
+ * gradient of the weight, dW = G^T . H).  B, transB, ldb, C, ldc as for
+ * tgemm_run; epilogue TGEMM_EPI_STORE_BF16 or TGEMM_EPI_STORE_F32.  Every
+ * shape runs on the matrix-core kernel (no pointwise, matrix-vector or
+ * split-K route).  The result equals, bit for bit, tgemm_run on the
+ * gradient the rescale pass writes.  Labels outside [0, V) subtract
+ * nothing.  Validation, errors, asynchrony and streams as for tgemm_run; a
+ * NULL scale or labels, or another epilogue, is TGEMM_ERR_INVALID_ARG.
+ */
+TGEMM_API int tgemm_run_ce_grad(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                const void* E, int64_t lde, const float* scale,
+                                const int32_t* labels, const void* B, int64_t ldb, void* C,
+                                int64_t ldc, int epilogue, void* stream);
+
+/*
  * The RoPE region of "Schedule a small matmul op as a reduction (or
  * pointwise) op" as far as that page's %kernel_math listing goes, in one
  * launch (the page's closing remark: the section fused into a single

@@ -10,6 +10,7 @@
 // which needs the row's final logsumexp, is finished by `ce_grad_fixup`
 // in a second pass instead of a cooperative launch.
 #include "bf16_cvt.h"
+#include "ce_grad.h"
 #include "tgemm_internal.h"
 
 namespace tgemm {
@@ -130,8 +131,8 @@ __global__ void __launch_bounds__(256) ce_grad_fixup_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int c = c0 + 2 * q;
-      float lo = from_bf16(w[q] & 0xffffu) * scale - (c == lab ? 1.f : 0.f);
-      float hi = from_bf16(w[q] >> 16) * scale - (c + 1 == lab ? 1.f : 0.f);
+      const float lo = ce_grad_value(w[q] & 0xffffu, scale, c == lab);
+      const float hi = ce_grad_value(w[q] >> 16, scale, c + 1 == lab);
       w[q] = pack_bf16x2(lo, hi);
     }
     *reinterpret_cast<uint4*>(g) = make_uint4(w[0], w[1], w[2], w[3]);
@@ -139,13 +140,35 @@ __global__ void __launch_bounds__(256) ce_grad_fixup_kernel(
     for (int e = 0; e < 8 && c0 + e < N; ++e) {
       const int c = c0 + e;
       const float scale = exp_f(pm[(int64_t)(c / blk_cols) * M + row] - l);
-      const float v = from_bf16(g[e]) * scale - (c == lab ? 1.f : 0.f);
-      g[e] = to_bf16(v);
+      g[e] = to_bf16(ce_grad_value(g[e], scale, c == lab));
     }
   }
 }
 
+// The exported scale table of the deferred gradient: s[c][m] = exp(m_b -
+// lse[m]) for every 64-column chunk c of row m (b = the CE block holding the
+// chunk: the same value for the chunks of one block), fp32 [nchunk][M].
+__global__ void __launch_bounds__(256) ce_scale_kernel(const float* __restrict__ pm,
+                                                       const float* __restrict__ lse, int M,
+                                                       int nchunk, int chunks_per_blk,
+                                                       float* __restrict__ scale) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)nchunk * M) return;
+  const int c = (int)(gid / M);
+  const int row = (int)(gid - (int64_t)c * M);
+  scale[gid] = exp_f(pm[(int64_t)(c / chunks_per_blk) * M + row] - lse[row]);
+}
+
 }  // namespace
+
+hipError_t launch_ce_scale(const float* part_m, const float* lse, int M, int N, int blk_cols,
+                           float* scale, hipStream_t s) {
+  const int nchunk = (N + kCeScaleCols - 1) / kCeScaleCols;
+  const int64_t threads = (int64_t)nchunk * M;
+  hipLaunchKernelGGL(ce_scale_kernel, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s,
+                     part_m, lse, M, nchunk, blk_cols / kCeScaleCols, scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_ce_combine(const float* part_m, const float* part_s, const float* ylabel,
                              const int32_t* labels, int M, int N, int nblk, float* loss,

@@ -271,7 +271,7 @@ namespace {
 int run_impl(WsMode mode, char transA, char transB, int64_t M, int64_t N, int64_t K,
              const void* A, int64_t lda, const void* B, int64_t ldb, void* C, int64_t ldc,
              int epilogue, const int32_t* labels, float* out_loss, void* out_grad,
-             hipStream_t s) {
+             hipStream_t s, float* out_scale = nullptr) {
   const int m = (int)M, n = (int)N, k = (int)K;
 
   // Element strides of the length-M / length-N vectors of a K=1 product.
@@ -409,7 +409,8 @@ int run_impl(WsMode mode, char transA, char transB, int64_t M, int64_t N, int64_
   }
 
   // Cross-entropy: GEMM + per-block partials, then the per-row combine,
-  // then (with a gradient) the rescale pass.
+  // then (with a gradient) the rescale pass -- or, for a deferred gradient
+  // (out_scale set), the scale table the backward GEMMs apply on load.
   if (out_grad != nullptr && ((M * ((N + 7) / 8) + 255) / 256) > kMaxWorkgroups)
     return TGEMM_ERR_UNSUPPORTED;
   const int blk = ce_block_cols(cfg);
@@ -428,7 +429,9 @@ int run_impl(WsMode mode, char transA, char transB, int64_t M, int64_t N, int64_
   hipError_t e = launch_gemm(transA, transB, cfg, kEpiCE, p, s);
   if (e == hipSuccess)
     e = launch_ce_combine(p.part_m, p.part_s, p.ylabel, labels, m, n, nblk, out_loss, lse, s);
-  if (e == hipSuccess && out_grad != nullptr)
+  if (e == hipSuccess && out_scale != nullptr)
+    e = launch_ce_scale(p.part_m, lse, m, n, blk, out_scale, s);
+  else if (e == hipSuccess && out_grad != nullptr)
     e = launch_ce_grad_fixup(p.grad, ldc, p.part_m, lse, labels, m, n, blk, s);
   const hipError_t ef = release_workspace(w, s);
   if (e == hipSuccess) e = ef;
@@ -461,6 +464,66 @@ extern "C" int tgemm_run_noalloc(char transA, char transB, int64_t M, int64_t N,
 }
 
 extern "C" int64_t tgemm_noalloc_scratch_bytes(void) { return (int64_t)kScratchBytes; }
+
+extern "C" int tgemm_run_ce_deferred(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                     const void* A, int64_t lda, const void* B, int64_t ldb,
+                                     const int32_t* labels, float* out_loss, void* out_e,
+                                     int64_t lde, float* out_scale, void* stream) {
+  if (out_e == nullptr || out_scale == nullptr) return TGEMM_ERR_INVALID_ARG;
+  const int st = tgemm_validate(transA, transB, M, N, K, A, lda, B, ldb, nullptr, lde,
+                                TGEMM_EPI_CE, labels, out_loss, out_e);
+  if (st != TGEMM_OK) return st;
+  // (a K = 1 product takes the pointwise path, which writes the finished
+  // gradient; there is no deferred form of it)
+  if (K == 1) return TGEMM_ERR_UNSUPPORTED;
+  return run_impl(kWsCached, transA, transB, M, N, K, A, lda, B, ldb, nullptr, lde, TGEMM_EPI_CE,
+                  labels, out_loss, out_e, reinterpret_cast<hipStream_t>(stream), out_scale);
+}
+
+extern "C" int tgemm_run_ce_grad(char transA, char transB, int64_t M, int64_t N, int64_t K,
+                                 const void* E, int64_t lde, const float* scale,
+                                 const int32_t* labels, const void* B, int64_t ldb, void* C,
+                                 int64_t ldc, int epilogue, void* stream) {
+  if (epilogue != TGEMM_EPI_STORE_BF16 && epilogue != TGEMM_EPI_STORE_F32)
+    return TGEMM_ERR_INVALID_ARG;
+  if (scale == nullptr || labels == nullptr) return TGEMM_ERR_INVALID_ARG;
+  const int st = tgemm_validate(transA, transB, M, N, K, E, lde, B, ldb, C, ldc, epilogue,
+                                nullptr, nullptr, nullptr);
+  if (st != TGEMM_OK) return st;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  // every shape on the matrix-core kernel (its loader applies the
+  // rescale), without a K split
+  int split = 1;
+  const int cfg = choose_tile(false, (int)M, (int)N, (int)K, TGEMM_EPI_CE, &split);
+  GemmParams p = {};
+  p.A = static_cast<const uint16_t*>(E);
+  p.B = static_cast<const uint16_t*>(B);
+  p.lda = lde;
+  p.ldb = ldb;
+  p.ldc = ldc;
+  p.M = (int)M;
+  p.N = (int)N;
+  p.K = (int)K;
+  p.tilesM = ceil_div(M, tile_rows(cfg));
+  p.tilesN = ceil_div(N, tile_cols(cfg));
+  p.splitk = 1;
+  p.kchunk = (int)K;
+  if ((int64_t)p.tilesM * p.tilesN > kMaxWorkgroups) return TGEMM_ERR_UNSUPPORTED;
+  p.groupM = p.tilesM < 4 ? p.tilesM : (p.tilesM <= 8 ? p.tilesM : 4);
+  p.aligned = ((reinterpret_cast<uintptr_t>(E) | reinterpret_cast<uintptr_t>(B)) & 15) == 0 &&
+              lde % 8 == 0 && ldb % 8 == 0;
+  p.C = C;
+  p.gscale = scale;
+  p.glabels = labels;
+  p.gtok = is_n(transA) ? (int)M : (int)K;
+  p.gvoc = is_n(transA) ? (int)K : (int)M;
+  if (verbose())
+    fprintf(stderr, "tgemm: ce grad gemm %c%c M=%lld N=%lld K=%lld tile=%d\n", transA, transB,
+            (long long)M, (long long)N, (long long)K, cfg);
+  return status_of(launch_gemm(transA, transB, cfg,
+                               epilogue == TGEMM_EPI_STORE_BF16 ? kEpiGStoreBf16 : kEpiGStoreF32,
+                               p, s));
+}
 
 extern "C" int tgemm_rope_region(const void* q, int64_t ldq, int64_t P, int64_t H, int64_t D,
                                  const int64_t* pos, int64_t spos, const float* inv_freq,

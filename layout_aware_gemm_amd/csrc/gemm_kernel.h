@@ -26,6 +26,7 @@
 #include <type_traits>
 
 #include "bf16_cvt.h"
+#include "ce_grad.h"
 #include "tgemm_internal.h"
 
 namespace tgemm {
@@ -107,6 +108,34 @@ __device__ __forceinline__ void q8_vec(uint4& v, float s) {
 #else
   (void)v, (void)s;
 #endif
+}
+
+// ----------------------------------------------------------------------
+// Cross-entropy gradient operand made on load: the 8 bf16 values of one
+// loaded vector are 8 consecutive vocabulary columns n0 .. n0+7 of token t
+// of the stored e = bf16(exp(y - m_b)); each becomes bf16(e * s - [label])
+// with s the scale of the token's 64-column chunk (ce_grad_value, the
+// arithmetic of the rescale pass, so the bits are the same).  Elements
+// outside the gradient (zero-filled edges) stay zero.
+// ----------------------------------------------------------------------
+// The scale of token t's chunk and the label's offset from n0 (-1: no
+// label column in this vector); zero-filled elements get scale 0.
+__device__ __forceinline__ void g_params(const GemmParams& p, int t, int n0, float& s, int& rel) {
+  s = 0.f;
+  rel = -1;
+  if (t < p.gtok && n0 < p.gvoc) {
+    s = p.gscale[(int64_t)(n0 / kCeScaleCols) * p.gtok + t];
+    rel = p.glabels[t] - n0;
+  }
+}
+
+__device__ __forceinline__ void g_vec(uint4& v, float s, int rel) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    w[q] = pack_bf16x2(ce_grad_value(w[q] & 0xffffu, s, rel == 2 * q),
+                       ce_grad_value(w[q] >> 16, s, rel == 2 * q + 1));
+  v = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
 // ----------------------------------------------------------------------
@@ -195,6 +224,21 @@ struct LoaderKMajor {
     for (int i = 0; i < L; ++i) q8_vec(v[i], sc);
   }
 
+  // A cross-entropy gradient with tokens along the rows (A 'N'): vector i
+  // holds 8 vocabulary columns (k) of token row r0 + i*NTH/8 + tid/8.  The
+  // scales and labels of a k-step are loaded with its panel (load_g) and
+  // applied one vector at a time (rescale_one).
+  float gs[L];
+  int gl[L];
+  __device__ __forceinline__ void load_g(const GemmParams& p, int r0, int k0, int tid) {
+#pragma unroll
+    for (int i = 0; i < L; ++i) {
+      const int q = tid + NTH * i;
+      g_params(p, r0 + (q >> 3), k0 + (q & 7) * 8, gs[i], gl[i]);
+    }
+  }
+  __device__ __forceinline__ void rescale_one(int i) { g_vec(v[i], gs[i], gl[i]); }
+
   // The store as U units (one 16-byte LDS write each), so that they can be
   // spread between matrix-core instructions.
   static constexpr int U = L;
@@ -275,6 +319,17 @@ struct LoaderMNMajor {
 #pragma unroll
     for (int j = 0; j < L; ++j) q8_vec(v[j], sc);
   }
+
+  // A cross-entropy gradient stored [tokens][vocabulary] and read 'T' (the
+  // GEMM's k is the token): vector j holds 8 vocabulary rows of token k.
+  float gs[L];
+  int gl[L];
+  __device__ __forceinline__ void load_g(const GemmParams& p, int r0, int k0, int tid) {
+    const int kb = tid % KBN, mc = tid / KBN;
+#pragma unroll
+    for (int j = 0; j < L; ++j) g_params(p, k0 + kb * L + j, r0 + mc * 8, gs[j], gl[j]);
+  }
+  __device__ __forceinline__ void rescale_one(int j) { g_vec(v[j], gs[j], gl[j]); }
 
   __device__ __forceinline__ uint32_t elem(int j, int i) const {
     return (u4comp(v[j], i >> 1) >> ((i & 1) * 16)) & 0xffffu;
@@ -540,14 +595,20 @@ __device__ __forceinline__ void plain_substep(f32x16_t (&acc)[FM][FN], const bf1
 // One k-substep of the register path: MFMA q, one fragment read of the
 // next substep (first FM+FN slots), and, when `st_on` is set, the LDS store
 // units of loaders `la` then `lb` (the next k-step's operand panels, into
-// `da` and `db`), spread evenly over the slots.
-template <int FM, int FN, bool SW, typename LdA, typename LdB>
+// `da` and `db`), spread evenly over the slots.  GA (A is a cross-entropy
+// gradient finished on load): B's units go first, and A's vectors are
+// transformed one per slot in the slots before A's first unit, as late as
+// possible after their loads were issued.
+template <int FM, int FN, bool SW, bool GA = false, typename LdA, typename LdB>
 __device__ __forceinline__ void store2_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
                                                const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
                                                const uint16_t* rd_stage, int a_base, int b_base,
-                                               int xo, const LdA& la, const LdB& lb, uint16_t* da,
+                                               int xo, LdA& la, const LdB& lb, uint16_t* da,
                                                uint16_t* db, int tid, bool st_on) {
   constexpr int SL = FM * FN, U = LdA::U + LdB::U;
+  // GA: the slot of A's first store unit; A's L vectors are transformed in
+  // the slots before it (all in slot 0 when it is slot 0)
+  constexpr int A0 = GA ? (LdB::U * SL) / U : 0;
   const uint16_t* pa = rd_stage + a_base + xo;
   const uint16_t* pb = rd_stage + b_base + xo;
 #pragma unroll
@@ -557,11 +618,21 @@ __device__ __forceinline__ void store2_substep(f32x16_t (&acc)[FM][FN], const bf
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
     if (st_on) {
-      // units u with floor(u * SL / U) == q
+      if constexpr (GA) {
+#pragma unroll
+        for (int v = 0; v < LdA::L; ++v)
+          if ((A0 > 0 ? (v * A0) / LdA::L : 0) == q) la.rescale_one(v);
+      }
+      // units u with floor(u * SL / U) == q (GA: B's units first)
 #pragma unroll
       for (int u = (q * U + SL - 1) / SL; u < U && (u * SL) / U == q; ++u) {
-        if (u < LdA::U) la.store_unit(da, tid, u);
-        else lb.store_unit(db, tid, u - LdA::U);
+        if constexpr (GA) {
+          if (u < LdB::U) lb.store_unit(db, tid, u);
+          else la.store_unit(da, tid, u - LdB::U);
+        } else {
+          if (u < LdA::U) la.store_unit(da, tid, u);
+          else lb.store_unit(db, tid, u - LdA::U);
+        }
       }
     }
     __builtin_amdgcn_sched_barrier(0);
@@ -802,7 +873,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
   // (Q8, OS: the sum times the output scale, one fp32 multiply)
   constexpr bool OS = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32 || EPI == kEpiOsBf16 ||
                       EPI == kEpiOsF32;
-  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32 || OS) {
+  constexpr bool GS = EPI == kEpiGStoreBf16 || EPI == kEpiGStoreF32;
+  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32 || OS || GS) {
     float os = 1.f;
     if constexpr (OS) os = p.qscales[2];
     // One output row at a time: its address is formed once, and the FN
@@ -812,7 +884,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
     const bool full = m0 + wr0 + 32 * FM <= p.M && n0 + wc0 + 32 * FN <= p.N;
     auto put = [&](int64_t off, float v) __attribute__((always_inline)) {
       if constexpr (OS) v = __fmul_rn(v, os);
-      if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16 || EPI == kEpiOsBf16)
+      if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiQ8Bf16 || EPI == kEpiOsBf16 ||
+                    EPI == kEpiGStoreBf16)
         reinterpret_cast<uint16_t*>(p.C)[off] = to_bf16(v);
       else
         reinterpret_cast<float*>(p.C)[off] = v;
@@ -1087,8 +1160,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr int RING = (BM + BN) * kRK * ring_stages<BM, BN>();
   constexpr bool SW = EPI == kEpiCE;  // transposed accumulators for row reductions
   constexpr bool Q8 = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32;  // e4m3fn operands made on load
+  constexpr bool GA = EPI == kEpiGStoreBf16 || EPI == kEpiGStoreF32;  // CE gradient A on load
   constexpr int LDS_ELEMS =
-      (A_KMAJOR && B_KMAJOR && !Q8 && RING > 2 * STAGE) ? RING : 2 * STAGE;
+      (A_KMAJOR && B_KMAJOR && !Q8 && !GA && RING > 2 * STAGE) ? RING : 2 * STAGE;
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
 
   const int tid = threadIdx.x;
@@ -1125,7 +1199,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
                         ((kend - kbeg) % kBK) == 0 && p.lda < (1 << 23) && p.ldb < (1 << 23);
   bool staged = false;  // main loop done on a global->LDS copy path
   // (the direct copies move raw bf16, so Q8 operands take the register path)
-  if constexpr (A_KMAJOR && B_KMAJOR && !Q8) {
+  if constexpr (A_KMAJOR && B_KMAJOR && !Q8 && !GA) {
     if (interior && BM == 256) {
       static_assert(BM != 256 || 2 * SA + 3 * SB <= LDS_ELEMS, "three B panels must fit");
       dma3_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
@@ -1139,7 +1213,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
   // (both operands K-contiguous without the cast: interior tiles always take
   // a direct-copy loop above, so this path is not compiled for them)
-  constexpr bool kRegInterior = !(A_KMAJOR && B_KMAJOR) || Q8;
+  constexpr bool kRegInterior = !(A_KMAJOR && B_KMAJOR) || Q8 || GA;
   if (kRegInterior && !staged && interior) {
     // Register path, interior tiles: one buffer load per 16-byte vector and
     // no bounds tests.  The loads of k-step kt+1 are issued right after the
@@ -1148,6 +1222,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     // unit per matrix-core instruction during the third substep of kt.
     typename LoaderSel<A_KMAJOR, BM>::type la;
     typename LoaderSel<B_KMAJOR, BN>::type lb;
+    using LA = typename LoaderSel<A_KMAJOR, BM>::type;
     const int nk = (kend - kbeg) / kBK;
     la.init_interior(p.lda, tid);
     lb.init_interior(p.ldb, tid);
@@ -1158,15 +1233,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     }
     la.load_interior(p.A, p.lda, m0, kbeg);
     lb.load_interior(p.B, p.ldb, n0, kbeg);
+    if constexpr (GA) la.load_g(p, m0, kbeg, tid);
     if constexpr (Q8) {
       la.quantize(qa);
       lb.quantize(qb);
+    }
+    if constexpr (GA) {
+#pragma unroll
+      for (int u = 0; u < LA::L; ++u) la.rescale_one(u);
     }
     la.store(lds, tid);
     lb.store(lds + SA, tid);
     if (nk > 1) {
       la.load_interior(p.A, p.lda, m0, kbeg + kBK);
       lb.load_interior(p.B, p.ldb, n0, kbeg + kBK);
+      if constexpr (GA) la.load_g(p, m0, kbeg + kBK, tid);
     }
     __syncthreads();
     bf16x8_t fa[2][FM], fb[2][FN];
@@ -1185,12 +1266,15 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
         }
       }
       plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
-      store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3], la,
-                                 lb, nx, nx + SA, tid, more);
+      // (GA: the next panel's gradient transform rides in this substep, just
+      // before its stores; its scales and labels came with the panel)
+      store2_substep<FM, FN, SW, GA>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3],
+                                     la, lb, nx, nx + SA, tid, more);
       __syncthreads();
       if (kt + 2 < nk) {
         la.load_interior(p.A, p.lda, m0, kbeg + (kt + 2) * kBK);
         lb.load_interior(p.B, p.ldb, n0, kbeg + (kt + 2) * kBK);
+        if constexpr (GA) la.load_g(p, m0, kbeg + (kt + 2) * kBK, tid);
       }
       // (in the last k-step this reads a stale stage that is never used)
       plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
@@ -1201,15 +1285,21 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     // needed) stores into the other LDS stage.
     typename LoaderSel<A_KMAJOR, BM>::type la;
     typename LoaderSel<B_KMAJOR, BN>::type lb;
+    using LA = typename LoaderSel<A_KMAJOR, BM>::type;
     const int nk = (kend - kbeg + kBK - 1) / kBK;
     la.load(p.A, p.lda, m0, p.M, kbeg, kend, aligned, tid);
     lb.load(p.B, p.ldb, n0, p.N, kbeg, kend, aligned, tid);
+    if constexpr (GA) la.load_g(p, m0, kbeg, tid);
     float qa = 0.f, qb = 0.f;
     if constexpr (Q8) {
       qa = p.qscales[0];
       qb = p.qscales[1];
       la.quantize(qa);
       lb.quantize(qb);
+    }
+    if constexpr (GA) {
+#pragma unroll
+      for (int u = 0; u < LA::L; ++u) la.rescale_one(u);
     }
     la.store(lds, tid);
     lb.store(lds + SA, tid);
@@ -1222,6 +1312,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       if (more) {
         la.load(p.A, p.lda, m0, p.M, kbeg + (kt + 1) * kBK, kend, aligned, tid);
         lb.load(p.B, p.ldb, n0, p.N, kbeg + (kt + 1) * kBK, kend, aligned, tid);
+        if constexpr (GA) la.load_g(p, m0, kbeg + (kt + 1) * kBK, tid);
       }
       const uint16_t* st = lds + cur * STAGE;
       uint16_t* nx = lds + (cur ^ 1) * STAGE;
@@ -1233,6 +1324,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
         if constexpr (Q8) {
           la.quantize(qa);
           lb.quantize(qb);
+        }
+        if constexpr (GA) {
+#pragma unroll
+          for (int u = 0; u < LA::L; ++u) la.rescale_one(u);
         }
         la.store(nx, tid);
         lb.store(nx + SA, tid);
@@ -1282,6 +1377,12 @@ hipError_t launch_gemm_tpl(int epi, const GemmParams& p, hipStream_t s) {
       break;
     case kEpiOsF32:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiOsF32>), grid, block, 0, s, p);
+      break;
+    case kEpiGStoreBf16:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiGStoreBf16>), grid, block, 0, s, p);
+      break;
+    case kEpiGStoreF32:
+      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiGStoreF32>), grid, block, 0, s, p);
       break;
     default:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiCE>), grid, block, 0, s, p);

@@ -19,7 +19,11 @@ enum EpiKind : int {
   kEpiQ8Bf16 = 3,
   kEpiQ8F32 = 4,
   kEpiOsBf16 = 5,
-  kEpiOsF32 = 6
+  kEpiOsF32 = 6,
+  // A is a cross-entropy gradient kept unscaled (see GemmParams::gscale):
+  // each loaded element of A becomes bf16(e * s - [label]) before use.
+  kEpiGStoreBf16 = 7,
+  kEpiGStoreF32 = 8
 };
 
 // Tile configurations of the GEMM kernel (k-step 64): BM x BN = 256x256 or
@@ -45,6 +49,14 @@ struct GemmParams {
   uint16_t* grad;     // optional [M][ldc] bf16: exp(y - block max), fixed up later
   // Q8 epilogues: device fp32 {scale_a, scale_b, out_scale}
   const float* qscales;
+  // G epilogues: operand A holds e = bf16(exp(y - m_b)) of a fused CE with
+  // gtok rows (tokens) and gvoc columns (vocabulary); row t's 64-column
+  // chunk c has the scale gscale[c * gtok + t] and the label glabels[t].
+  // With A 'N' the GEMM's rows are tokens and its k the vocabulary; with
+  // A 'T' the other way round.
+  const float* gscale;
+  const int32_t* glabels;
+  int gtok, gvoc;
 };
 
 // Width (in columns) of the per-row partial blocks the CE epilogue writes.
@@ -81,6 +93,9 @@ hipError_t launch_gemv(int shape, const uint16_t* X, int64_t ldx, int64_t sx, co
 hipError_t launch_ce_combine(const float* part_m, const float* part_s, const float* ylabel,
                              const int32_t* labels, int M, int N, int nblk, float* loss,
                              float* lse, hipStream_t s);
+// The deferred gradient's scale table, fp32 [ceil(N/64)][M] (ce.hip).
+hipError_t launch_ce_scale(const float* part_m, const float* lse, int M, int N, int blk_cols,
+                           float* scale, hipStream_t s);
 hipError_t launch_ce_grad_fixup(uint16_t* grad, int64_t ldc, const float* part_m,
                                 const float* lse, const int32_t* labels, int M, int N,
                                 int blk_cols, hipStream_t s);

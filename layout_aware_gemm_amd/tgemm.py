@@ -34,7 +34,8 @@ EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
            "tgemm_status_string", "tgemm_set_tile_config", "tgemm_set_split_k",
            "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version",
            "tgemm_release_workspace", "tgemm_run_noalloc", "tgemm_noalloc_scratch_bytes",
-           "tgemm_rope_region", "tgemm_validate_rope_region")
+           "tgemm_rope_region", "tgemm_validate_rope_region", "tgemm_run_ce_deferred",
+           "tgemm_run_ce_grad")
 
 
 class TgemmError(RuntimeError):
@@ -87,6 +88,12 @@ def lib():
         L.tgemm_run_noalloc.restype = ctypes.c_int
         L.tgemm_noalloc_scratch_bytes.argtypes = []
         L.tgemm_noalloc_scratch_bytes.restype = ctypes.c_int64
+        L.tgemm_run_ce_deferred.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64, vp, i64,
+                                            vp, i64, vp, vp, vp, i64, vp, vp]
+        L.tgemm_run_ce_deferred.restype = ctypes.c_int
+        L.tgemm_run_ce_grad.argtypes = [ctypes.c_char, ctypes.c_char, i64, i64, i64, vp, i64, vp,
+                                        vp, vp, i64, vp, i64, ctypes.c_int, vp]
+        L.tgemm_run_ce_grad.restype = ctypes.c_int
         L.tgemm_rope_region.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64, vp, vp]
         L.tgemm_rope_region.restype = ctypes.c_int
         L.tgemm_validate_rope_region.argtypes = [vp, i64, i64, i64, i64, vp, i64, vp, vp, vp, i64,
@@ -373,6 +380,72 @@ def rope_cos_sin(pos, inv_freq, stream=None):
     run("N", tb, P, F, 1, pos, pos.stride(0), inv_freq, ldb, cos, 2 * F, EPI_ROPE_COSSIN,
         out_grad=sin, stream=stream)
     return cos, sin
+
+
+def run_ce_deferred(transA, transB, M, N, K, A, lda, B, ldb, labels, out_loss, out_e, lde,
+                    out_scale, stream=None, check=True):
+    """Call ``tgemm_run_ce_deferred``."""
+    dev = A.device if isinstance(A, torch.Tensor) and A.is_cuda else None
+    st = lib().tgemm_run_ce_deferred(_flag(transA), _flag(transB), int(M), int(N), int(K),
+                                     _ptr(A), int(lda), _ptr(B), int(ldb), _ptr(labels),
+                                     _ptr(out_loss), _ptr(out_e), int(lde), _ptr(out_scale),
+                                     _stream(stream, dev))
+    if check and st != TGEMM_OK:
+        raise TgemmError(st, "tgemm_run_ce_deferred")
+    return st
+
+
+def run_ce_grad(transA, transB, M, N, K, E, lde, scale, labels, B, ldb, C, ldc, epilogue,
+                stream=None, check=True):
+    """Call ``tgemm_run_ce_grad``."""
+    dev = E.device if isinstance(E, torch.Tensor) and E.is_cuda else None
+    st = lib().tgemm_run_ce_grad(_flag(transA), _flag(transB), int(M), int(N), int(K), _ptr(E),
+                                 int(lde), _ptr(scale), _ptr(labels), _ptr(B), int(ldb), _ptr(C),
+                                 int(ldc), int(epilogue), _stream(stream, dev))
+    if check and st != TGEMM_OK:
+        raise TgemmError(st, "tgemm_run_ce_grad")
+    return st
+
+
+def cross_entropy_deferred(h, w, labels, stream=None):
+    """As ``cross_entropy(h, w, labels, grad=True)`` but with the gradient
+    left unscaled: returns (loss fp32 [M], e bf16 [M, N], scale fp32
+    [ceil(N/64), M]); ``ce_grad_matmul`` finishes the gradient on load."""
+    if h.dtype != torch.bfloat16 or w.dtype != torch.bfloat16:
+        raise TypeError("cross_entropy_deferred expects bf16 operands")
+    M, K = h.shape
+    K2, N = w.shape
+    if K != K2:
+        raise ValueError("inner dimensions differ")
+    if labels.dtype != torch.int32 or labels.shape != (M,) or not labels.is_contiguous():
+        raise ValueError("labels must be a contiguous int32 [M] tensor")
+    _check_dev(h, w, labels)
+    ta, lda = layout_of(h)
+    tb, ldb = layout_of(w)
+    loss = torch.empty(M, dtype=torch.float32, device=h.device)
+    e = torch.empty(M, N, dtype=torch.bfloat16, device=h.device)
+    scale = torch.empty((N + 63) // 64, M, dtype=torch.float32, device=h.device)
+    run_ce_deferred(ta, tb, M, N, K, h, lda, w, ldb, labels, loss, e, N, scale, stream=stream)
+    return loss, e, scale
+
+
+def ce_grad_matmul(g, scale, labels, b, out_dtype=torch.bfloat16, stream=None):
+    """op(G) @ b where G is the gradient of ``cross_entropy_deferred``,
+    finished as it is loaded.  ``g`` is its e tensor [T, V] for G, or
+    ``e.t()`` for G^T; ``b`` any row/column-major view."""
+    if g.dtype != torch.bfloat16 or b.dtype != torch.bfloat16:
+        raise TypeError("ce_grad_matmul expects bf16 operands")
+    _check_dev(g, b, scale, labels)
+    M, K = g.shape
+    K2, N = b.shape
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    ta, lda = layout_of(g)
+    tb, ldb = layout_of(b)
+    out = torch.empty(M, N, dtype=out_dtype, device=g.device)
+    epi = EPI_STORE_BF16 if out_dtype == torch.bfloat16 else EPI_STORE_F32
+    run_ce_grad(ta, tb, M, N, K, g, lda, scale, labels, b, ldb, out, N, epi, stream=stream)
+    return out
 
 
 def run_rope_region(q, ldq, P, H, D, pos, spos, inv_freq, cos, sin, ldc, q_out, stream=None,

@@ -101,3 +101,14 @@ def rms_rel_err(gpu, ref):
         return 0.0
     rms = float(np.sqrt(np.mean(ref * ref)))
     return float(np.max(np.abs(gpu - ref) / (np.abs(ref) + rms / 64.0)))
+
+
+def backward_bound_ratio(got, g_ref, other, ref):
+    """Worst ratio of |got - ref| to the bound the arithmetic allows, for a
+    product ref = g_ref @ other of a gradient with the oracle's (one bf16
+    rounding of softmax - onehot): the GPU gradient differs from it by at
+    most two roundings, 2^-8 relative per element, so the product by at most
+    2^-8 (|g_ref| @ |other|); the bf16 output adds 2^-9 |ref|.  The bound is
+    taken at twice that."""
+    bound = 2.0 ** -7 * (np.abs(g_ref) @ np.abs(other)) + 2.0 ** -8 * np.abs(ref) + 1e-30
+    return float(np.max(np.abs(got - ref) / bound))

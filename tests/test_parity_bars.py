@@ -14,8 +14,8 @@ import numpy as np
 
 import oracle
 import workloads
-from parity_util import (GEMM_BF16_TOL, GEMM_REL_TOL, grad_check, rms_rel_err, sample_rows,
-                         scaled_err)
+from parity_util import (GEMM_BF16_TOL, GEMM_REL_TOL, backward_bound_ratio, grad_check,
+                         rms_rel_err, sample_rows, scaled_err)
 
 
 def onehot_of(labels, N):
@@ -112,3 +112,28 @@ def test_layout_sweep_bar_rejects_scaled_or_shifted_products():
     # every wrong answer by far
     for wrong in (0.85 * ref, 0.98 * ref, np.roll(ref, 1, axis=1), ref[::-1]):
         assert rms_rel_err(wrong, ref) > 4 * GEMM_REL_TOL
+
+
+def test_backward_bound_rejects_wrong_products():
+    """The bound used for the CE backward GEMMs (2^-7 |G| @ |W| + 2^-8 |ref|)
+    passes the product of the gradient after two bf16 roundings and rejects
+    a gradient that ignores the logits, a scaled one, and a product with the
+    wrong operand order."""
+    rng = np.random.default_rng(1)
+    M, V, K = 64, 300, 48
+    y = rng.normal(size=(M, V)) * 2
+    labels = rng.integers(0, V, M)
+    W = rng.normal(size=(V, K)) * 0.2
+    _, grad, _ = oracle.cross_entropy(y, labels)
+    g1 = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(grad))
+    ref = g1 @ W
+    oh = onehot_of(labels, V)
+    p = grad + oh
+    g2 = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(
+        oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(p * (1 + 2.0 ** -9))) - oh))
+    got = oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(g2 @ W))
+    assert backward_bound_ratio(got, g1, W, ref) <= 1.0
+    uniform = (np.full((M, V), 1.0 / V) - oh) @ W
+    assert backward_bound_ratio(uniform, g1, W, ref) > 4.0
+    assert backward_bound_ratio(0.9 * ref, g1, W, ref) > 4.0
+    assert backward_bound_ratio(np.roll(ref, 1, axis=0), g1, W, ref) > 4.0
