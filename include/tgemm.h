@@ -194,11 +194,8 @@ TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int
  * pointwise(input); output2 = transpose(output1)", the example: before a
  * float8 linear each input element is scaled, clamped to the largest
  * finite e4m3fn value and cast to e4m3fn, and the page's pattern also
- * writes a transposed copy of the fp8 tensor.  Here the GEMM's loader
- * applies the scale, clamp and cast to each element as it reads the bf16
- * operand in its stored layout, or, for large products, a pass casts each
- * operand once into a workspace copy in its own layout: no transposed copy
- * is ever written.)
+ * writes a transposed copy of the fp8 tensor.  Here no transposed copy is
+ * ever stored: the operands are read in their stored layouts.)
  *
  *   transA, transB, M, N, K, A, lda, B, ldb, C, ldc: as for tgemm_run with
  *                   a STORE epilogue; A and B are bf16 in any layout.
@@ -212,18 +209,21 @@ TGEMM_API int tgemm_validate(char transA, char transB, int64_t M, int64_t N, int
  * C = out_scale * sum_k qA[m,k] * qB[k,n], products exact, fp32
  * accumulation, one fp32 multiply by out_scale, then the store epilogue
  * (bf16 with round-to-nearest-even, or fp32).  Pass out_scale =
- * 1 / (scale_a * scale_b) to undo both casts.  The products run on the
- * bf16 matrix cores, which hold every e4m3fn value exactly.
+ * 1 / (scale_a * scale_b) to undo both casts.
  *
  * Large products (at least two 256-row and two 256-column tiles, every
- * stored row 16-byte aligned with a multiple of 8 elements) may instead
- * cast each operand once, with the same arithmetic, into a compact bf16
- * copy in its own layout (never transposed) in the library's per-stream
- * workspace, and multiply the copies: the same bits, fewer casts.  See
- * tgemm_set_fp8_cast_once.
- *
- * If the workspace for the copies cannot be allocated, the product casts
- * on load instead.
+ * stored row 16-byte aligned with a multiple of 8 elements) cast each
+ * operand once into a K-contiguous matrix of e4m3fn codes (one byte each,
+ * zero-padded to whole tiles) in the library's per-stream workspace, and
+ * multiply the codes on the fp8 matrix cores (v_mfma_f32_32x32x64_f8f6f4).
+ * Other products cast each element as the GEMM loads it and multiply on
+ * the bf16 matrix cores, which hold every e4m3fn value exactly.  Both
+ * routes multiply the same e4m3fn values with fp32 accumulation; their
+ * sums may differ in the last bits (the matrix cores group the k
+ * differently), and both are exact where every partial sum is exactly
+ * representable (e.g. integer-valued operands).  tgemm_set_fp8_cast_once(0)
+ * forces the cast on load.  If the workspace for the codes cannot be
+ * allocated, the product casts on load.
  *
  * Validation, errors, asynchrony and streams as for tgemm_run.  Returns
  * TGEMM_OK or a negative tgemm_status; an unsupported epilogue or a NULL
@@ -351,9 +351,11 @@ TGEMM_API int tgemm_set_split_k(int split);
 /*
  * Tuning / testing knob for tgemm_run_fp8: 1 (default) lets large products
  * (at least two 256-row and two 256-column tiles, 16-byte rows) cast each
- * operand once, in a pass of its own, into a compact copy in its own layout
- * in the library's per-stream workspace, before the GEMM; 0 always casts
- * on load.  Both routes give the same bits.  Returns the previous value,
+ * operand once, in a pass of its own, into K-contiguous e4m3fn codes in the
+ * library's per-stream workspace and multiply them on the fp8 matrix
+ * cores; 0 always casts on load (bf16 matrix cores).  Both routes multiply
+ * the same e4m3fn values; their fp32 sums may differ in the last bits.
+ * Returns the previous value,
  * or TGEMM_ERR_INVALID_ARG for anything but 0 or 1.  Not thread-safe with
  * concurrent tgemm_run_fp8 calls.
  */

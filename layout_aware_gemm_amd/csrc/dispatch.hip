@@ -543,14 +543,16 @@ extern "C" int tgemm_rope_region(const void* q, int64_t ldq, int64_t P, int64_t 
 }
 
 // fp8 (e4m3fn) operands.  No K split, no matrix-vector or K = 1 shortcut:
-// every element goes through the cast.  Two routes with the same bits:
-//  - cast on load, on the GEMM kernel's register path (the direct copies
-//    would move raw bf16);
-//  - cast once: when both tile counts are at least 2 (so the loader would
-//    cast each element at least twice) and the operands allow 16-byte rows,
-//    a pass casts each operand into a compact copy in its own layout in the
-//    per-stream workspace, and the GEMM reads the copies as plain bf16 (the
-//    direct copies for K-contiguous operands) and applies the output scale.
+// every element goes through the cast.  Two routes multiply the same
+// e4m3fn values:
+//  - packed (the default for large products: both tile counts at least 2,
+//    every stored row 16-byte aligned with a multiple of 8 elements): a
+//    pass casts each operand once into a K-contiguous code matrix, zero-
+//    padded to whole tiles, in the per-stream workspace, and the fp8
+//    matrix-core kernel multiplies the codes and applies the output scale;
+//  - cast on load, on the bf16 kernel's register path (bf16 matrix cores,
+//    each code widened back to bf16, which holds it exactly): small or
+//    unaligned products, or when the workspace cannot be had.
 extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int64_t K,
                              const void* A, int64_t lda, const void* B, int64_t ldb, void* C,
                              int64_t ldc, int epilogue, const float* scales, void* stream) {
@@ -584,35 +586,43 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
   p.C = C;
   p.qscales = scales;
   const bool bf16_out = epilogue == TGEMM_EPI_STORE_BF16;
-  const int64_t rowsA = is_n(transA) ? M : K, colsA = is_n(transA) ? K : M;
-  const int64_t rowsB = is_n(transB) ? K : N, colsB = is_n(transB) ? N : K;
-  const bool cast_once = g_fp8_cast_once && p.aligned && colsA % 8 == 0 && colsB % 8 == 0 &&
-                         ceil_div(M, 256) >= 2 && ceil_div(N, 256) >= 2;
+  // the stored rows' lengths (the contiguous axis)
+  const int64_t colsA = is_n(transA) ? K : M, colsB = is_n(transB) ? N : K;
+  const int BT = tile_rows(cfg);
+  const int64_t Mp = (int64_t)ceil_div(M, BT) * BT, Np = (int64_t)ceil_div(N, BT) * BT;
+  const int64_t Kp = (K + 127) / 128 * 128;
+  const bool packed = g_fp8_cast_once && p.aligned && colsA % 8 == 0 && colsB % 8 == 0 &&
+                      ceil_div(M, 256) >= 2 && ceil_div(N, 256) >= 2 && Kp / 2 < (1 << 23);
   if (verbose())
     fprintf(stderr,
             "tgemm: fp8 gemm %c%c M=%lld N=%lld K=%lld tile=%d grid=%dx%d aligned=%d "
-            "cast_once=%d\n",
+            "packed=%d\n",
             transA, transB, (long long)M, (long long)N, (long long)K, cfg, p.tilesM, p.tilesN,
-            p.aligned, cast_once ? 1 : 0);
-  // the two copies, B's at a 256-byte boundary; without the memory for
-  // them the product casts on load instead (same bits, no workspace)
-  const size_t bytesA = (size_t)rowsA * (size_t)colsA * 2;
+            p.aligned, packed ? 1 : 0);
+  // the two code matrices, B's at a 256-byte boundary; without the memory
+  // for them the product casts on load instead
+  const size_t bytesA = (size_t)Mp * (size_t)Kp;
   const size_t offB = (bytesA + 255) / 256 * 256;
   Workspace w;
-  if (!cast_once ||
-      get_workspace(kWsCached, s, offB + (size_t)rowsB * (size_t)colsB * 2, &w) != TGEMM_OK)
+  if (!packed || get_workspace(kWsCached, s, offB + (size_t)Np * (size_t)Kp, &w) != TGEMM_OK)
     return status_of(
         launch_gemm(transA, transB, cfg, bf16_out ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
-  uint16_t* qa = static_cast<uint16_t*>(w.ptr);
-  uint16_t* qb = reinterpret_cast<uint16_t*>(static_cast<char*>(w.ptr) + offB);
-  hipError_t e = launch_q8_cast(p.A, lda, rowsA, colsA, scales, qa, s);
-  if (e == hipSuccess) e = launch_q8_cast(p.B, ldb, rowsB, colsB, scales + 1, qb, s);
+  uint8_t* qa = static_cast<uint8_t*>(w.ptr);
+  uint8_t* qb = static_cast<uint8_t*>(w.ptr) + offB;
+  hipError_t e = launch_q8_pack(p.A, lda, is_n(transA), (int)M, (int)K, scales, qa, (int)Mp,
+                                (int)Kp, s);
+  if (e == hipSuccess)
+    e = launch_q8_pack(p.B, ldb, !is_n(transB), (int)N, (int)K, scales + 1, qb, (int)Np, (int)Kp,
+                       s);
   if (e == hipSuccess) {
-    p.A = qa;
-    p.B = qb;
-    p.lda = colsA;
-    p.ldb = colsB;
-    e = launch_gemm(transA, transB, cfg, bf16_out ? kEpiOsBf16 : kEpiOsF32, p, s);
+    p.A = reinterpret_cast<const uint16_t*>(qa);
+    p.B = reinterpret_cast<const uint16_t*>(qb);
+    p.lda = p.ldb = Kp / 2;
+    p.K = (int)(Kp / 2);
+    p.kchunk = p.K;
+    p.tilesM = (int)(Mp / BT);
+    p.tilesN = (int)(Np / BT);
+    e = launch_gemm_f8(cfg, bf16_out ? kEpiOsBf16 : kEpiOsF32, p, s);
   }
   const hipError_t r = release_workspace(w, s);
   return status_of(e != hipSuccess ? e : r);

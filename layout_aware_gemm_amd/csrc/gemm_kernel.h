@@ -85,10 +85,10 @@ __device__ __forceinline__ uint32_t hi_halves(f32x2_t f) {
 }
 #endif
 
-// Cast the 8 bf16 values of one loaded 16-byte vector: two packed
-// conversions fill one register with four e4m3fn codes, and each register
-// converts back as two pairs.
-__device__ __forceinline__ void q8_vec(uint4& v, float s) {
+// The e4m3fn codes of the 8 bf16 values of one 16-byte vector: two packed
+// conversions fill one register with four codes (x: elements 0-3, y: 4-7,
+// element e in byte e % 4).
+__device__ __forceinline__ uint2 q8_codes(const uint4& v, float s) {
 #if defined(__HIP_DEVICE_COMPILE__)
   const uint32_t w[4] = {v.x, v.y, v.z, v.w};
   int c[2];
@@ -101,10 +101,22 @@ __device__ __forceinline__ void q8_vec(uint4& v, float s) {
     c[h] = __builtin_amdgcn_cvt_pk_fp8_f32(q8_scaled(b << 16, s), q8_scaled(b & 0xffff0000u, s),
                                            t, true);
   }
-  v.x = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[0], false));
-  v.y = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[0], true));
-  v.z = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[1], false));
-  v.w = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8(c[1], true));
+  return make_uint2((uint32_t)c[0], (uint32_t)c[1]);
+#else
+  (void)v, (void)s;
+  return make_uint2(0, 0);
+#endif
+}
+
+// Cast the 8 bf16 values of one loaded 16-byte vector in place: the codes
+// of q8_codes, each register converted back as two pairs.
+__device__ __forceinline__ void q8_vec(uint4& v, float s) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  const uint2 c = q8_codes(v, s);
+  v.x = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, false));
+  v.y = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8((int)c.x, true));
+  v.z = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, false));
+  v.w = hi_halves(__builtin_amdgcn_cvt_pk_f32_fp8((int)c.y, true));
 #else
   (void)v, (void)s;
 #endif
@@ -1372,21 +1384,17 @@ hipError_t launch_gemm_tpl(int epi, const GemmParams& p, hipStream_t s) {
     case kEpiQ8F32:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiQ8F32>), grid, block, 0, s, p);
       break;
-    case kEpiOsBf16:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiOsBf16>), grid, block, 0, s, p);
-      break;
-    case kEpiOsF32:
-      hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiOsF32>), grid, block, 0, s, p);
-      break;
     case kEpiGStoreBf16:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiGStoreBf16>), grid, block, 0, s, p);
       break;
     case kEpiGStoreF32:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiGStoreF32>), grid, block, 0, s, p);
       break;
-    default:
+    case kEpiCE:
       hipLaunchKernelGGL((gemm_kernel<BM, BN, AK, BK, kEpiCE>), grid, block, 0, s, p);
       break;
+    default:  // (the OS epilogues belong to the fp8 kernel)
+      return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }

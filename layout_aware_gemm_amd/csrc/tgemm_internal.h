@@ -10,8 +10,8 @@ namespace tgemm {
 // Epilogue variants of the matrix-core GEMM kernel.  The Q8 stores take
 // operands cast to e4m3fn on load (scale, clamp, round) and multiply the
 // sum by the output scale before storing.  The OS stores multiply by the
-// output scale too, on operands that a separate pass already cast
-// (launch_q8_cast), so their loads are plain bf16.
+// output scale too, after the fp8 matrix-core kernel (launch_gemm_f8)
+// multiplied codes that a separate pass cast (launch_q8_pack).
 enum EpiKind : int {
   kEpiStoreBf16 = 0,
   kEpiStoreF32 = 1,
@@ -124,10 +124,19 @@ hipError_t launch_k1_ce(const uint16_t* a, int64_t sa, const uint16_t* b, int64_
                         int N, const int32_t* labels, float* loss, uint16_t* grad, int64_t ldg,
                         hipStream_t s);
 
-// e4m3fn cast (scale[0], clamp, round; the values kept as bf16) of a
-// row-major [rows, cols] operand with row stride ld into a compact
-// [rows, cols] copy.  X 16-byte aligned, ld % 8 == 0, cols % 8 == 0.
-hipError_t launch_q8_cast(const uint16_t* X, int64_t ld, int64_t rows, int64_t cols,
-                          const float* scale, uint16_t* out, hipStream_t s);
+// e4m3fn cast (scale[0], clamp, round) of an fp8 GEMM operand into the
+// K-contiguous code matrix out [Rp][Kp] (one byte per code, zero past R
+// rows and K columns) that launch_gemm_f8 reads (defined in fp8_cast.hip).
+// k_contiguous: X is [R][K] with row stride ld (K % 8 == 0); otherwise X is
+// [K][R] with row stride ld (R % 8 == 0).  X 16-byte aligned, ld % 8 == 0,
+// Rp % 64 == 0, Kp % 128 == 0.
+hipError_t launch_q8_pack(const uint16_t* X, int64_t ld, bool k_contiguous, int R, int K,
+                          const float* scale, uint8_t* out, int Rp, int Kp, hipStream_t s);
+
+// fp8 matrix-core GEMM over two packed code matrices (defined in
+// gemm_f8.hip): p.A [tilesM*BM][2*p.K] and p.B [tilesN*BN][2*p.K] bytes
+// passed as 16-bit units (p.lda = p.ldb = p.K, p.K % 64 == 0), an OS
+// epilogue, C [p.M][p.N].  cfg: kTile256 or kTile128.
+hipError_t launch_gemm_f8(int cfg, int epi, const GemmParams& p, hipStream_t s);
 
 }  // namespace tgemm

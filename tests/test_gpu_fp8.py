@@ -1,12 +1,22 @@
 """GPU parity of the fp8 (e4m3fn) operand GEMM (tgemm_run_fp8) against the
 oracle, through the C-ABI.
 
-Each bf16 operand element is scaled, clamped and cast to e4m3fn as the
-kernel loads it; the products of e4m3fn values are exact, so the only
-rounding on the GPU is the fp32 accumulation and the output scale.
-Integer-valued cases are therefore exact (bitwise), and random cases are
-held to the fp32 summation bound: |error| <= K * 2^-24 * sum |qa qb| (to
-first order), times the output scale, plus one rounding of the product.
+Each bf16 operand element is scaled, clamped and cast to e4m3fn; the
+products of e4m3fn values are exact, so the only rounding on the GPU is in
+the sums and the output scale.  Two routes:
+  - cast on load (bf16 matrix cores): held to the fp32 summation bound,
+    |error| <= K * 2^-24 * sum |qa qb| (to first order), times the output
+    scale, plus one rounding of the product;
+  - packed (fp8 matrix cores, v_mfma_f32_32x32x64_f8f6f4): that bound plus
+    the matrix core's own group sums.  Measured on MI355X with structured
+    inputs: it adds the products of each group of 8 consecutive k at the
+    magnitude of the group's largest product, truncating the bits of the
+    others below about 2^-12 of it (448 + 7 * 2^-6 gives 448; 65536 + 7 * 1
+    gives 65536; groups combine without that loss; subnormal codes are
+    exact).  So each group of 8 adds at most 2^-9 * max |qa qb| over the
+    group (8 truncated products, each short of one 2^-12 unit).
+Integer-valued cases whose group sums stay within that precision are exact
+(bitwise) on both routes.
 """
 
 import numpy as np
@@ -16,7 +26,8 @@ import torch
 import oracle
 import workloads
 from layout_aware_gemm_amd import tgemm
-from parity_util import GEMM_BF16_TOL, bf16_to_f64, bits, dev, scaled_err
+from parity_util import (FP8_RMS_BF16, FP8_RMS_F32, GEMM_BF16_TOL, bf16_to_f64, bits, dev,
+                         fp8_error_bound as error_bound, rms_ratio, scaled_err, within_bound)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,19 +54,13 @@ def ref_of(d, ta, tb, M, N, K, scales, rows=None):
                            workloads.bf16_bits(d["B"]).reshape(-1), d["ldb"], *scales, rows=rows)
 
 
-def abs_products(d, ta, tb, M, N, K, scales, rows=None):
-    """out_scale * sum_k |qa qb| in fp64 (the summation bound)."""
-    sa, sb, so = scales
-    qa = np.abs(oracle.quantize(d["opA"].float().numpy(), sa))
-    qb = np.abs(oracle.quantize(d["opB"].float().numpy(), sb))
-    if rows is not None:
-        qa = qa[np.asarray(rows)]
-    return (qa @ qb) * abs(so)
-
-
-def within_f32_bound(C, ref, absprod, K):
-    bound = K * 2.0 ** -24 * absprod * 1.01 + np.abs(ref) * 2.0 ** -23 + 1e-30
-    return np.all(np.abs(C - ref) <= bound)
+def takes_packed_route(d, ta, tb, M, N, K):
+    """tgemm_run_fp8's packed route: at least two 256-row and two 256-column
+    tiles, 16-byte rows (the test tensors are aligned)."""
+    colsA = K if ta == "N" else M
+    colsB = N if tb == "N" else K
+    return (-(-M // 256) >= 2 and -(-N // 256) >= 2 and d["lda"] % 8 == 0
+            and d["ldb"] % 8 == 0 and colsA % 8 == 0 and colsB % 8 == 0)
 
 
 SHAPES = [(64, 48, 64), (300, 260, 200), (257, 129, 100), (1, 50, 70), (40, 1, 33), (33, 17, 1),
@@ -82,15 +87,20 @@ def test_integer_valued_is_exact(M, N, K, ta, tb):
 def test_scale_clamp_round_against_oracle(M, N, K, ta, tb):
     """N(0, 30) inputs times 10 and 0.05: most of op(A) clamps to +-448, op(B)
     lands on the whole e4m3fn range including subnormals; fp32 output within
-    the summation bound, and the bf16 output is the fp32 one rounded once."""
+    the route's bound, and the bf16 output is the fp32 one rounded once."""
     d = workloads.random_operands(M, N, K, ta, tb, seed=11 * M + N + K, std=30.0)
     scales = (10.0, 0.05, 1.0 / 0.5)
+    packed = takes_packed_route(d, ta, tb, M, N, K)
     Cf = run(d, ta, tb, M, N, K, scales).cpu().numpy().astype(np.float64)
     ref = ref_of(d, ta, tb, M, N, K, scales)
-    assert within_f32_bound(Cf, ref, abs_products(d, ta, tb, M, N, K, scales), K)
+    bound = error_bound(d, scales, K, ref, packed=packed)
+    assert within_bound(Cf, ref, bound)
+    assert rms_ratio(Cf, ref) <= FP8_RMS_F32
     Cb = run(d, ta, tb, M, N, K, scales, out_dtype=torch.bfloat16)
     assert np.array_equal(bits(Cb), oracle.f64_to_bf16_bits(Cf))
-    assert scaled_err(bf16_to_f64(Cb), ref) <= GEMM_BF16_TOL
+    assert within_bound(bf16_to_f64(Cb), ref, bound + np.abs(ref) * 2.0 ** -8)
+    if not packed:
+        assert scaled_err(bf16_to_f64(Cb), ref) <= GEMM_BF16_TOL
 
 
 def test_nan_propagates_through_the_cast():
@@ -113,13 +123,15 @@ def test_nan_propagates_through_the_cast():
         assert nan.sum() == N + M - 1
         ref = ref_of(d2, ta, tb, M, N, K, scales)
         ok = ~nan
-        absprod = abs_products(d2, ta, tb, M, N, K, scales)
-        assert within_f32_bound(C[ok].astype(np.float64), ref[ok], absprod[ok], K)
+        bound = error_bound(d2, scales, K, np.nan_to_num(ref))
+        assert within_bound(C[ok].astype(np.float64), ref[ok], bound[ok])
 
 
 # at least two 256-row and two 256-column tiles, every stored row a multiple
-# of 8 elements: these take the cast-once route (a cast pass into a compact
-# copy, then the GEMM on plain bf16) unless it is switched off
+# of 8 elements: these take the packed route (a pass casts each operand into
+# K-contiguous e4m3fn codes, the fp8 matrix cores multiply them) unless it
+# is switched off, which casts on load and multiplies on the bf16 matrix
+# cores
 CAST_ONCE = [(600, 520, 1000), (520, 536, 136), (1024, 768, 512)]
 
 
@@ -134,32 +146,36 @@ def run_route(d, ta, tb, M, N, K, scales, cast_once, **kw):
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", CAST_ONCE)
 def test_cast_once_route(M, N, K, ta, tb):
-    """Integer-valued inputs: the oracle's bits.  Random inputs: the same
-    bits as casting on load, in fp32 and bf16, and within the fp32 bound."""
+    """Both routes, every layout, ragged K and ragged tiles (the pack's zero
+    padding): integer-valued inputs give the oracle's bits; random inputs,
+    unclamped and with op(A) clamping and op(B) reaching subnormals, are
+    within the route's bound on sampled rows, and the bf16 output is the
+    route's fp32 output rounded once."""
     d = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K, int_range=8)
     assert d["lda"] % 8 == 0 and d["ldb"] % 8 == 0
     scales = (0.5, 2.0, 0.25)
-    C = run_route(d, ta, tb, M, N, K, scales, 1)
-    assert np.array_equal(C.cpu().numpy().astype(np.float64), ref_of(d, ta, tb, M, N, K, scales))
-    r = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K + 1, std=3.0)
-    scales = (4.0, 8.0, 1.0 / 32)
-    for dt in (torch.float32, torch.bfloat16):
-        once = run_route(r, ta, tb, M, N, K, scales, 1, out_dtype=dt)
-        load = run_route(r, ta, tb, M, N, K, scales, 0, out_dtype=dt)
-        if dt == torch.bfloat16:
-            assert np.array_equal(bits(once), bits(load))
-        else:
-            assert torch.equal(once, load)
+    ref = ref_of(d, ta, tb, M, N, K, scales)
+    for route in (1, 0):
+        C = run_route(d, ta, tb, M, N, K, scales, route)
+        assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
     rows = [0, 1, M // 2, M - 1]
-    once_f32 = run_route(r, ta, tb, M, N, K, scales, 1)
-    ref = ref_of(r, ta, tb, M, N, K, scales, rows=rows)
-    absprod = abs_products(r, ta, tb, M, N, K, scales, rows=rows)
-    assert within_f32_bound(once_f32.cpu().numpy()[rows].astype(np.float64), ref, absprod, K)
+    for std, scales in ((3.0, (4.0, 8.0, 1.0 / 32)), (30.0, (10.0, 0.05, 2.0))):
+        r = workloads.random_operands(M, N, K, ta, tb, seed=M + N + K + int(std), std=std)
+        ref = ref_of(r, ta, tb, M, N, K, scales, rows=rows)
+        for route in (1, 0):
+            bound = error_bound(r, scales, K, ref, rows=rows, packed=route == 1)
+            Cf = run_route(r, ta, tb, M, N, K, scales, route)
+            assert within_bound(Cf.cpu().numpy()[rows].astype(np.float64), ref, bound)
+            assert rms_ratio(Cf.cpu().numpy()[rows], ref) <= FP8_RMS_F32
+            Cb = run_route(r, ta, tb, M, N, K, scales, route, out_dtype=torch.bfloat16)
+            assert np.array_equal(bits(Cb), oracle.f64_to_bf16_bits(
+                Cf.cpu().numpy().astype(np.float64)))
 
 
 def test_cast_once_keeps_nan():
-    """A NaN element survives the cast pass: its row and column are NaN, the
-    rest equals the cast-on-load route bit for bit."""
+    """A NaN element survives the pack: its row and column are NaN, like the
+    oracle's, and the sampled rows' other entries are within the route's
+    bound."""
     M, N, K = 520, 536, 256
     d = workloads.random_operands(M, N, K, "N", "T", seed=41, std=2.0)
     opA, opB = d["opA"].clone(), d["opB"].clone()
@@ -168,18 +184,25 @@ def test_cast_once_keeps_nan():
     sa_, lda = workloads.store_operand(opA, "N")
     sb_, ldb = workloads.store_operand(opB, "T")
     d2 = {"opA": opA, "opB": opB, "A": sa_, "lda": lda, "B": sb_, "ldb": ldb}
-    once = run_route(d2, "N", "T", M, N, K, (1.0, 1.0, 1.0), 1)
-    load = run_route(d2, "N", "T", M, N, K, (1.0, 1.0, 1.0), 0)
-    nan = torch.isnan(once)
-    assert nan[5, :].all() and nan[:, 300].all() and int(nan.sum()) == M + N - 1
-    assert torch.equal(torch.isnan(load), nan)
-    assert torch.equal(once[~nan], load[~nan])
+    scales = (1.0, 1.0, 1.0)
+    for route in (1, 0):
+        C = run_route(d2, "N", "T", M, N, K, scales, route)
+        nan = torch.isnan(C)
+        assert nan[5, :].all() and nan[:, 300].all() and int(nan.sum()) == M + N - 1
+        rows = [0, 5, 200, M - 1]
+        ref = ref_of(d2, "N", "T", M, N, K, scales, rows=rows)
+        got = C.cpu().numpy()[rows].astype(np.float64)
+        assert np.array_equal(np.isnan(got), np.isnan(ref))
+        ok = ~np.isnan(ref)
+        bound = error_bound(d2, scales, K, np.nan_to_num(ref), rows=rows, packed=route == 1)
+        assert np.all(np.abs(got - ref)[ok] <= bound[ok])
 
 
 @pytest.mark.parametrize("cfg", [1, 2])
 def test_layouts_and_tiles_give_the_same_bits(cfg):
-    """The cast happens before the (layout-independent) LDS image, so all
-    four layouts, and both tile configurations, give identical bits."""
+    """The cast happens before the (layout-independent) image the matrix
+    cores read -- the packed codes here -- so all four layouts, and both
+    tile configurations, give identical bits."""
     M, N, K = 384, 320, 448
     outs = []
     for ta, tb in LAYOUTS:
@@ -198,7 +221,8 @@ def test_fp8_linear_full_size(tb):
     [3072, 4096] weight (scale 1000), read in place ('T') or from its
     [4096, 3072] transposed storage ('N') -- the layout the page's pattern
     writes a transposed fp8 copy for.  bf16 output with the inverse scales,
-    24 sampled rows against the oracle."""
+    24 sampled rows against the oracle, within the packed route's bound plus
+    one bf16 rounding."""
     w = workloads.fp8_linear()
     M, K, N = 4096, 4096, 3072
     W = w["W"] if tb == "T" else w["W"].t().contiguous()
@@ -207,7 +231,12 @@ def test_fp8_linear_full_size(tb):
     C = run(d, "N", tb, M, N, K, scales, out_dtype=torch.bfloat16)
     rows = np.random.default_rng(8).choice(M, 24, replace=False)
     ref = ref_of(d, "N", tb, M, N, K, scales, rows=rows)
-    assert scaled_err(bf16_to_f64(C)[rows], ref) <= GEMM_BF16_TOL
+    d["opA"] = w["X"]
+    d["opB"] = w["W"].t()
+    assert takes_packed_route(d, "N", tb, M, N, K)
+    bound = error_bound(d, scales, K, ref, rows=rows, packed=True) + np.abs(ref) * 2.0 ** -8
+    assert within_bound(bf16_to_f64(C)[rows], ref, bound)
+    assert rms_ratio(bf16_to_f64(C)[rows], ref) <= FP8_RMS_BF16
     # and the fp8 product really differs from the bf16 one (the cast happened)
     plain = oracle.gemm("N", tb, M, N, K, workloads.bf16_bits(d["A"]).reshape(-1), d["lda"],
                         workloads.bf16_bits(d["B"]).reshape(-1), d["ldb"], rows=rows)

@@ -14,8 +14,9 @@ import numpy as np
 
 import oracle
 import workloads
-from parity_util import (GEMM_BF16_TOL, GEMM_REL_TOL, backward_bound_ratio, grad_check,
-                         rms_rel_err, sample_rows, scaled_err)
+from parity_util import (FP8_RMS_BF16, FP8_RMS_F32, GEMM_BF16_TOL, GEMM_REL_TOL,
+                         backward_bound_ratio, fp8_error_bound, grad_check, rms_ratio,
+                         rms_rel_err, sample_rows, scaled_err, within_bound)
 
 
 def onehot_of(labels, N):
@@ -137,3 +138,56 @@ def test_backward_bound_rejects_wrong_products():
     assert backward_bound_ratio(uniform, g1, W, ref) > 4.0
     assert backward_bound_ratio(0.9 * ref, g1, W, ref) > 4.0
     assert backward_bound_ratio(np.roll(ref, 1, axis=0), g1, W, ref) > 4.0
+
+
+def group_truncated_sum(qa, qb, shift):
+    """A plausible fp8 matrix-core result: in each group of 8 consecutive k,
+    every product truncated toward zero to a multiple of 2^(E - shift), E the
+    exponent of the group's largest |product|; exact sums otherwise."""
+    R, K = qa.shape
+    p = qa[:, :, None] * qb[None, :, :]
+    p = p.reshape(R, K // 8, 8, -1)
+    mx = np.abs(p).max(axis=2, keepdims=True)
+    u = 2.0 ** (np.floor(np.log2(np.where(mx > 0, mx, 1.0))) - shift)
+    return (np.trunc(p / u) * u).sum(axis=(1, 2))
+
+
+def test_fp8_packed_bars_reject_wrong_products():
+    """The fp8 packed route's checks (per-element bound with the group loss,
+    and the RMS ratio) pass the oracle's product and products truncated as
+    the fp8 matrix cores do (at the measured 2^-12 and at twice that), in
+    fp32 and after a bf16 rounding, and reject a 0.99x product, one group of
+    8 k left out, shifted columns and the e4m3fn cast skipped."""
+    rng = np.random.default_rng(4)
+    R, K, N = 6, 512, 192
+    x = rng.normal(size=(R, K))
+    w = rng.normal(size=(K, N)) * 0.02
+    sa, sb = 10.0, 1000.0
+    so = 1.0 / (sa * sb)
+    import torch
+    d = {"opA": torch.tensor(x), "opB": torch.tensor(w)}
+    qa, qb = oracle.quantize(x, sa), oracle.quantize(w, sb)
+    ref = (qa @ qb) * so
+    bound = fp8_error_bound(d, (sa, sb, so), K, ref, packed=True)
+
+    def bf16(v):
+        return oracle.bf16_bits_to_f64(oracle.f64_to_bf16_bits(v))
+
+    for shift in (12, 11):
+        got = group_truncated_sum(qa, qb, shift) * so
+        assert within_bound(got, ref, bound) and rms_ratio(got, ref) <= FP8_RMS_F32
+        gb = bf16(got)
+        assert within_bound(gb, ref, bound + np.abs(ref) * 2.0 ** -8)
+        assert rms_ratio(gb, ref) <= FP8_RMS_BF16
+    gap = qa.copy()
+    gap[:, 64:72] = 0
+    wrong = {
+        "scaled": 0.99 * ref,
+        "group left out": (gap @ qb) * so,
+        "shifted columns": np.roll(ref, 1, axis=1),
+        "no cast": (x * sa) @ (w * sb) * so,
+    }
+    for name, v in wrong.items():
+        assert not within_bound(v, ref, bound), name
+        assert rms_ratio(v, ref) > 4 * FP8_RMS_F32, name
+        assert rms_ratio(bf16(v), ref) > 2 * FP8_RMS_BF16, name
