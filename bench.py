@@ -27,7 +27,7 @@ PEAK_BF16_TFLOPS = 2516.6   # 256 CUs x 2.4 GHz x 4096 dense bf16 flop/clk/CU (p
 PEAK_HBM_GBS = 8000.0       # HBM3E, 8 TB/s
 PEAK_FP8_TFLOPS = 5033.2    # dense fp8: twice the bf16 rate per clock (published 5.0 PF)
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "nt_gemm_768x5120x13824_hbm_traffic.md")
-KERNEL_SOURCES = ["gemm_kernel.h", "gemm_nt.hip", "tgemm_internal.h", "dispatch.hip",
+KERNEL_SOURCES = ["gemm_kernel.h", "gemm_nt.hip", "tgemm_internal.h", "dispatch.hip", "ce_grad.h",
                   "splitk.hip", "bf16_cvt.h"]
 COPY_CAL_BYTES = 2 ** 30  # plain device copy used to calibrate the HBM byte counters
 
@@ -296,6 +296,55 @@ def rope_tables(steps, warmup):
     return out
 
 
+def fp8_linear(K_, W_):
+    """The float8 linear 4096x3072x4096 through tgemm_run_fp8 (cast passes
+    plus the fp8 matrix-core GEMM), the weight read in place (NT) and from
+    its transposed storage (NN); the bf16 product of the same shape; and
+    torch's unfused cast and transposed copy of the input, for context."""
+    import torch
+
+    import workloads
+    from layout_aware_gemm_amd import tgemm
+
+    dev = torch.device("cuda:0")
+    secondary = {}
+    wf = workloads.fp8_linear()
+    Xf, Wf = wf["X"].to(dev), wf["W"].to(dev)              # [4096, 4096], [3072, 4096]
+    Wft = wf["W"].t().contiguous().to(dev)                 # [4096, 3072]
+    sx, sw = wf["scale_x"], wf["scale_w"]
+    sc = torch.tensor([sx, sw, 1.0 / (sx * sw)], dtype=torch.float32, device=dev)
+    del wf
+    Yf = torch.empty(4096, 3072, dtype=torch.bfloat16, device=dev)
+    f8fl = 2.0 * 4096 * 3072 * 4096
+    for name, tb_, Bm, ldb_ in (("fp8_linear_4096x3072x4096_NT", "T", Wf, 4096),
+                                ("fp8_linear_4096x3072x4096_NN", "N", Wft, 3072)):
+        msf = time_stream(lambda i: tgemm.run_fp8("N", tb_, 4096, 3072, 4096, Xf, 4096, Bm,
+                                                  ldb_, Yf, 3072, tgemm.EPI_STORE_BF16, sc),
+                          K_, W_, 1)
+        secondary[f"{name}_us"] = round(msf * 1e3, 2)
+        secondary[f"{name}_tflops"] = round(f8fl / (msf * 1e-3) / 1e12, 2)
+        # the packed route: cast passes plus the GEMM on the fp8 matrix cores
+        secondary[f"{name}_frac_of_fp8_peak"] = round(
+            f8fl / (msf * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
+    # the same product in bf16 (the unquantized operands), for comparison
+    msb = time_stream(lambda i: tgemm.run("N", "T", 4096, 3072, 4096, Xf, 4096, Wf, 4096, Yf,
+                                          3072, tgemm.EPI_STORE_BF16), K_, W_, 1)
+    secondary["bf16_linear_4096x3072x4096_NT_us"] = round(msb * 1e3, 2)
+    # context: the page's unfused pattern (scale, clamp and cast, then the
+    # transposed fp8 copy) for the input alone, in torch, before any GEMM
+    sxt = sc[0:1]
+
+    def unfused_cast(i):
+        t = (Xf * sxt).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
+        return t.t().contiguous().t()
+
+    msu = time_stream(unfused_cast, K_, W_, 1)
+    secondary["fp8_cast_and_transposed_copy_torch_us"] = round(msu * 1e3, 2)
+    del Xf, Wf, Wft, Yf, sc
+
+    return secondary
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -313,6 +362,9 @@ def main():
     ap.add_argument("--only-rope", action="store_true",
                     help="time only the K=1 RoPE table (4096 and 256 x 4096 positions) and print "
                          "its figures (a profiling command; no headline line)")
+    ap.add_argument("--only-fp8", action="store_true",
+                    help="time only the fp8 linear 4096x3072x4096 (NT, NN) and the bf16 product "
+                         "of its shape, and print the figures (a profiling command)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE; "
@@ -349,6 +401,9 @@ def main():
     if args.only_ce:
         out, *_ = fused_ce(K_, W_)
         print(json.dumps(out), flush=True)
+        return 0
+    if args.only_fp8:
+        print(json.dumps(fp8_linear(K_, W_)), flush=True)
         return 0
     if args.only_sweep:
         log("timing the 4096^3 layout sweep ...")
@@ -462,40 +517,7 @@ def main():
         secondary["dot_1e8_frac_of_hbm"] = round(4 * Kd / (msd * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
         del av, bv, cd
 
-        # ---- fp8 (e4m3fn) operands: the float8 linear -----------------------
-        wf = workloads.fp8_linear()
-        Xf, Wf = wf["X"].to(dev), wf["W"].to(dev)              # [4096, 4096], [3072, 4096]
-        Wft = wf["W"].t().contiguous().to(dev)                 # [4096, 3072]
-        sx, sw = wf["scale_x"], wf["scale_w"]
-        sc = torch.tensor([sx, sw, 1.0 / (sx * sw)], dtype=torch.float32, device=dev)
-        del wf
-        Yf = torch.empty(4096, 3072, dtype=torch.bfloat16, device=dev)
-        f8fl = 2.0 * 4096 * 3072 * 4096
-        for name, tb_, Bm, ldb_ in (("fp8_linear_4096x3072x4096_NT", "T", Wf, 4096),
-                                    ("fp8_linear_4096x3072x4096_NN", "N", Wft, 3072)):
-            msf = time_stream(lambda i: tgemm.run_fp8("N", tb_, 4096, 3072, 4096, Xf, 4096, Bm,
-                                                      ldb_, Yf, 3072, tgemm.EPI_STORE_BF16, sc),
-                              K_, W_, 1)
-            secondary[f"{name}_us"] = round(msf * 1e3, 2)
-            secondary[f"{name}_tflops"] = round(f8fl / (msf * 1e-3) / 1e12, 2)
-            # the packed route: cast passes plus the GEMM on the fp8 matrix cores
-            secondary[f"{name}_frac_of_fp8_peak"] = round(
-                f8fl / (msf * 1e-3) / 1e12 / PEAK_FP8_TFLOPS, 4)
-        # the same product in bf16 (the unquantized operands), for comparison
-        msb = time_stream(lambda i: tgemm.run("N", "T", 4096, 3072, 4096, Xf, 4096, Wf, 4096, Yf,
-                                              3072, tgemm.EPI_STORE_BF16), K_, W_, 1)
-        secondary["bf16_linear_4096x3072x4096_NT_us"] = round(msb * 1e3, 2)
-        # context: the page's unfused pattern (scale, clamp and cast, then the
-        # transposed fp8 copy) for the input alone, in torch, before any GEMM
-        sxt = sc[0:1]
-
-        def unfused_cast(i):
-            t = (Xf * sxt).clamp(-448.0, 448.0).to(torch.float8_e4m3fn)
-            return t.t().contiguous().t()
-
-        msu = time_stream(unfused_cast, K_, W_, 1)
-        secondary["fp8_cast_and_transposed_copy_torch_us"] = round(msu * 1e3, 2)
-        del Xf, Wf, Wft, Yf, sc
+        secondary.update(fp8_linear(K_, W_))
 
         # ---- K=1 RoPE table --------------------------------------------------
         secondary.update(rope_tables(K_, W_))

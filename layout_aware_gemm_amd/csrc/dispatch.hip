@@ -67,7 +67,14 @@ int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
       cfg = kTile256;
       s = (int)auto_s;
     } else {
-      cfg = kTile128;
+      // A 128x128 tile does about 0.56x the work per compute unit of a
+      // 256x256 one on NT, so 256x256 tiles win once they fill about half
+      // the chip; the register-path layouts gain less from the big tile.
+      // (Measured at K = 4096, 256 against 128 tiles: NT 4096x3072 96 vs
+      // 131 us, 2048x4096 75 vs 78 us; NN / TN / TT at 144 tiles 129 / 159
+      // / 146 vs 146 / 199 / 147 us, at 128 tiles 126 / 157 / 144 vs 89 /
+      // 121 / 90 us.)
+      cfg = t256 >= (nt ? 128 : 144) ? kTile256 : kTile128;
     }
   }
   if (g_forced_split > 0) s = g_forced_split;

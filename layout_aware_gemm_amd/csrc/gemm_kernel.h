@@ -29,6 +29,10 @@
 #include "ce_grad.h"
 #include "tgemm_internal.h"
 
+#ifndef TGEMM_MIX
+#define TGEMM_MIX 1
+#endif
+
 namespace tgemm {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -1162,6 +1166,127 @@ __device__ __forceinline__ void dma3_mainloop(const GemmParams& p, int m0, int n
 }
 
 // ----------------------------------------------------------------------
+// Mixed staging for interior 256x256 tiles with exactly one K-contiguous
+// operand (NN: A; TT: B).  That operand (D) goes global -> LDS with the
+// direct copies into three panel buffers, the copies of k-step kt+2 issued
+// during substep 0 of kt, as in the three-buffer loop.  The other operand
+// (G, contiguous along M or N) is loaded into registers in two sets: the
+// set holding k-step kt+1 is transposed into one of two LDS panels during
+// substep 2 of kt and, after the barrier, receives k-step kt+3 -- seven
+// substeps of matrix-core work for its loads to arrive, where a single set
+// leaves three.  LDS: 3 + 2 panels of 32 KB.
+// ----------------------------------------------------------------------
+
+// One substep of the mixed loop: MFMA q, one fragment read of the next
+// substep (first FM+FN slots), this wave's copies of one D panel when `cp`
+// (one every SL/NCP slots), and the G set's LDS store units when `st`
+// (one every SL/U slots).
+template <int FM, int FN, int R, bool SW, typename LG>
+__device__ __forceinline__ void mix_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                            const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                            const uint16_t* pa, const uint16_t* pb, bool cp,
+                                            const DmaPanel<R>& d, const uint16_t* o,
+                                            uint16_t* ddst, int wave_u, bool st, const LG& g,
+                                            uint16_t* gdst, int tid) {
+  constexpr int SL = FM * FN;
+  constexpr int NCP = DmaPanel<R>::PER_WAVE;
+  static_assert(SL % NCP == 0 && SL % LG::U == 0, "side work must divide the slots evenly");
+#pragma unroll
+  for (int q = 0; q < SL; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    if (cp && q % (SL / NCP) == 0) d.issue_one(o, ddst, wave_u, q / (SL / NCP));
+    if (st && q % (SL / LG::U) == 0) g.store_unit(gdst, tid, q / (SL / LG::U));
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// k-steps [k0/64, k0/64 + nk), nk even; AK: A is the K-contiguous operand
+// (else B).
+template <int BM, int BN, int FM, int FN, bool AK, bool SW>
+__device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
+                                             uint16_t* lds, int tid, int wave, int lane,
+                                             int a_base, int b_local, const int* xo,
+                                             f32x16_t (&acc)[FM][FN]) {
+  static_assert(BM == BN, "one panel size for both operands");
+  constexpr int SP = BM * kBK;
+  constexpr int ND = DmaPanel<BM>::PER_WAVE;
+  using LG = LoaderMNMajor<BM>;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  uint16_t* const dbuf = lds;           // three D panels
+  uint16_t* const gbuf = lds + 3 * SP;  // two G panels
+  DmaPanel<BM> dp;
+  dp.init(AK ? p.lda : p.ldb, wave, lane);
+  const uint16_t* od = AK ? p.A + (int64_t)m0 * p.lda + k0 : p.B + (int64_t)n0 * p.ldb + k0;
+  const uint16_t* XG = AK ? p.B : p.A;
+  const int64_t ldg = AK ? p.ldb : p.lda;
+  const int rg0 = AK ? n0 : m0;
+  LG g0, g1;
+  g0.init_interior(ldg, tid);
+  g1.init_interior(ldg, tid);
+  // k-steps past the end re-read k-step 0 (never stored or multiplied), so
+  // every k-step issues the same loads and the wait counts stay fixed
+  auto kof = [nk](int t) { return (t < nk ? t : 0) * kBK; };
+  // fragment rows: A's panel base + a_base, B's + b_local
+  auto pa_of = [&](uint16_t* d, uint16_t* g) { return (AK ? d : g) + a_base; };
+  auto pb_of = [&](uint16_t* d, uint16_t* g) { return (AK ? g : d) + b_local; };
+  dp.issue(od + kof(0), dbuf, wave_u);
+  g0.load_interior(XG, ldg, rg0, k0 + kof(0));
+  dp.issue(od + kof(1), dbuf + SP, wave_u);
+  g1.load_interior(XG, ldg, rg0, k0 + kof(1));
+  g0.store(gbuf, tid);
+  g0.load_interior(XG, ldg, rg0, k0 + kof(2));
+  // D(0) landed (issued first; the rest may be in flight: G(0) done, D(1),
+  // G(1), G(2)); the G(0) stores done; other waves: the barrier
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(ND + 2 * LG::L, 0));
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  bf16x8_t fa[2][FM], fb[2][FN];
+  read_frags<FM, FN>(dbuf, AK ? a_base : b_local, (AK ? b_local : a_base) + 3 * SP, xo[0],
+                     AK ? fa[0] : fb[0], AK ? fb[0] : fa[0]);
+  // k-step kt; g holds k-step kt+1 and then receives kt+3
+  auto step = [&](LG& g, int kt) __attribute__((always_inline)) {
+    const int d3 = kt % 3, d3n = (kt + 1) % 3, d3p = (kt + 2) % 3;
+    uint16_t* dc = dbuf + d3 * SP;
+    uint16_t* gc = gbuf + (kt & 1) * SP;
+    uint16_t* dn = dbuf + d3n * SP;
+    uint16_t* gn = gbuf + ((kt + 1) & 1) * SP;
+    const bool more = kt + 1 < nk;
+    const uint16_t* pa = pa_of(dc, gc);
+    const uint16_t* pb = pb_of(dc, gc);
+    __builtin_amdgcn_sched_barrier(0);
+    mix_substep<FM, FN, BM, SW>(acc, fa[0], fb[0], fa[1], fb[1], pa + xo[1], pb + xo[1], true, dp,
+                                od + kof(kt + 2), dbuf + d3p * SP, wave_u, false, g, gn, tid);
+    mix_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], pa + xo[2], pb + xo[2], false,
+                                dp, od, dbuf, wave_u, false, g, gn, tid);
+    mix_substep<FM, FN, BM, SW>(acc, fa[0], fb[0], fa[1], fb[1], pa + xo[3], pb + xo[3], false,
+                                dp, od, dbuf, wave_u, more, g, gn, tid);
+    // D(kt+1) landed (after its copies: G(kt+2)'s loads and D(kt+2)'s
+    // copies), the G stores and this wave's fragment reads done; after the
+    // barrier no wave reads D(kt) or G(kt) any more
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(LG::L + ND, 0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    g.load_interior(XG, ldg, rg0, k0 + kof(kt + 3));
+    mix_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], pa_of(dn, gn) + xo[0],
+                                pb_of(dn, gn) + xo[0], false, dp, od, dbuf, wave_u, false, g, gn,
+                                tid);
+  };
+  // nk is even: the body is two unconditional steps (a conditional second
+  // step, or a second exit, merges two versions of the accumulators, which
+  // the register allocator does not keep in place)
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(g1, kt);
+    step(g0, kt + 1);
+  }
+  // the trailing loads must land before the LDS is reused or released
+  wait_dma();
+  __syncthreads();
+}
+
+// ----------------------------------------------------------------------
 // The kernel.
 // ----------------------------------------------------------------------
 template <int BM, int BN, bool A_KMAJOR, bool B_KMAJOR, int EPI>
@@ -1173,8 +1298,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr bool SW = EPI == kEpiCE;  // transposed accumulators for row reductions
   constexpr bool Q8 = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32;  // e4m3fn operands made on load
   constexpr bool GA = EPI == kEpiGStoreBf16 || EPI == kEpiGStoreF32;  // CE gradient A on load
+  // one K-contiguous operand, 256x256: the mixed loop (three D + two G panels)
+  constexpr bool MIX = TGEMM_MIX && (A_KMAJOR != B_KMAJOR) && BM == 256 && BN == 256 && !Q8 && !GA;
   constexpr int LDS_ELEMS =
-      (A_KMAJOR && B_KMAJOR && !Q8 && !GA && RING > 2 * STAGE) ? RING : 2 * STAGE;
+      MIX ? 2 * SA + 3 * SB
+          : ((A_KMAJOR && B_KMAJOR && !Q8 && !GA && RING > 2 * STAGE) ? RING : 2 * STAGE);
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
 
   const int tid = threadIdx.x;
@@ -1223,9 +1351,19 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       staged = true;
     }
   }
+  if constexpr (MIX) {
+    if (interior && ((kend - kbeg) / kBK) % 2 == 0) {
+      mix_mainloop<BM, BN, FM, FN, A_KMAJOR, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, tid,
+                                                 wave, lane, a_base, b_base - SA, xo, acc);
+      staged = true;
+    }
+  }
   // (both operands K-contiguous without the cast: interior tiles always take
   // a direct-copy loop above, so this path is not compiled for them)
-  constexpr bool kRegInterior = !(A_KMAJOR && B_KMAJOR) || Q8 || GA;
+  // (with the mixed loop compiled, an interior tile with an odd k-step count
+  // takes the general path: a third main loop merging its accumulators into
+  // the epilogue makes the register allocator spill there)
+  constexpr bool kRegInterior = (!(A_KMAJOR && B_KMAJOR) || Q8 || GA) && !MIX;
   if (kRegInterior && !staged && interior) {
     // Register path, interior tiles: one buffer load per 16-byte vector and
     // no bounds tests.  The loads of k-step kt+1 are issued right after the
