@@ -1203,20 +1203,21 @@ __device__ __forceinline__ void mix_substep(f32x16_t (&acc)[FM][FN], const bf16x
   }
 }
 
-// k-steps [k0/64, k0/64 + nk), nk even; AK: A is the K-contiguous operand
-// (else B).
+// k-steps [k0/64, k0/64 + nk); AK: A is the K-contiguous operand (else B).
 template <int BM, int BN, int FM, int FN, bool AK, bool SW>
 __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
-                                             uint16_t* lds, int tid, int wave, int lane,
-                                             int a_base, int b_local, const int* xo,
+                                             uint16_t* __restrict__ dbuf,
+                                             uint16_t* __restrict__ gbuf, int tid, int wave,
+                                             int lane, int a_base, int b_local, const int* xo,
                                              f32x16_t (&acc)[FM][FN]) {
+  // dbuf: three D panels; gbuf: two G panels.  They do not overlap, and
+  // saying so lets the compiler write G into LDS without first waiting for
+  // every direct copy in flight (which only write D's panels).
   static_assert(BM == BN, "one panel size for both operands");
   constexpr int SP = BM * kBK;
   constexpr int ND = DmaPanel<BM>::PER_WAVE;
   using LG = LoaderMNMajor<BM>;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  uint16_t* const dbuf = lds;           // three D panels
-  uint16_t* const gbuf = lds + 3 * SP;  // two G panels
   DmaPanel<BM> dp;
   dp.init(AK ? p.lda : p.ldb, wave, lane);
   const uint16_t* od = AK ? p.A + (int64_t)m0 * p.lda + k0 : p.B + (int64_t)n0 * p.ldb + k0;
@@ -1232,20 +1233,37 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
   // fragment rows: A's panel base + a_base, B's + b_local
   auto pa_of = [&](uint16_t* d, uint16_t* g) { return (AK ? d : g) + a_base; };
   auto pb_of = [&](uint16_t* d, uint16_t* g) { return (AK ? g : d) + b_local; };
-  dp.issue(od + kof(0), dbuf, wave_u);
-  g0.load_interior(XG, ldg, rg0, k0 + kof(0));
-  dp.issue(od + kof(1), dbuf + SP, wave_u);
-  g1.load_interior(XG, ldg, rg0, k0 + kof(1));
-  g0.store(gbuf, tid);
-  g0.load_interior(XG, ldg, rg0, k0 + kof(2));
+  // The step of k-step kt takes the set holding kt+1: g1 for even kt when
+  // nk is even.  With nk odd, k-step 0 runs before the loop on g0, so the
+  // loop's steps still come in pairs (g1, g0) and the sets swap roles here.
+  const bool odd = nk & 1;
+  auto prologue = [&](LG& s0, LG& s1) __attribute__((always_inline)) {
+    // s0 carries k-step 0, then k-step 2; s1 carries k-step 1
+    dp.issue(od + kof(0), dbuf, wave_u);
+    s0.load_interior(XG, ldg, rg0, k0 + kof(0));
+    dp.issue(od + kof(1), dbuf + SP, wave_u);
+    s1.load_interior(XG, ldg, rg0, k0 + kof(1));
+    s0.store(gbuf, tid);
+    s0.load_interior(XG, ldg, rg0, k0 + kof(2));
+  };
+  if (odd)
+    prologue(g1, g0);
+  else
+    prologue(g0, g1);
   // D(0) landed (issued first; the rest may be in flight: G(0) done, D(1),
   // G(1), G(2)); the G(0) stores done; other waves: the barrier
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(ND + 2 * LG::L, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   bf16x8_t fa[2][FM], fb[2][FN];
-  read_frags<FM, FN>(dbuf, AK ? a_base : b_local, (AK ? b_local : a_base) + 3 * SP, xo[0],
-                     AK ? fa[0] : fb[0], AK ? fb[0] : fa[0]);
+  {
+    const uint16_t* pa = pa_of(dbuf, gbuf) + xo[0];
+    const uint16_t* pb = pb_of(dbuf, gbuf) + xo[0];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) fa[0][i] = *reinterpret_cast<const bf16x8_t*>(pa + i * 32 * kBK);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) fb[0][j] = *reinterpret_cast<const bf16x8_t*>(pb + j * 32 * kBK);
+  }
   // k-step kt; g holds k-step kt+1 and then receives kt+3
   auto step = [&](LG& g, int kt) __attribute__((always_inline)) {
     const int d3 = kt % 3, d3n = (kt + 1) % 3, d3p = (kt + 2) % 3;
@@ -1274,16 +1292,99 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
                                 pb_of(dn, gn) + xo[0], false, dp, od, dbuf, wave_u, false, g, gn,
                                 tid);
   };
-  // nk is even: the body is two unconditional steps (a conditional second
-  // step, or a second exit, merges two versions of the accumulators, which
-  // the register allocator does not keep in place)
-  for (int kt = 0; kt < nk; kt += 2) {
+  // the body is two unconditional steps (a conditional second step, or a
+  // second exit, merges two versions of the accumulators inside the loop,
+  // which the register allocator does not keep in place)
+  int kt0 = 0;
+  if (odd) {
+    step(g0, 0);
+    kt0 = 1;
+  }
+  for (int kt = kt0; kt < nk; kt += 2) {
     step(g1, kt);
     step(g0, kt + 1);
   }
   // the trailing loads must land before the LDS is reused or released
   wait_dma();
   __syncthreads();
+}
+
+// ----------------------------------------------------------------------
+// Two register sets per operand, for interior 256x256 tiles with both
+// operands contiguous along M or N (TN), which the direct copies cannot
+// stage.  The sets holding k-step kt+1 are transposed into the other LDS
+// stage during substep 2 of kt and, after the barrier, receive k-step
+// kt+3: seven substeps for their loads to arrive, where one set per operand
+// leaves three.
+// ----------------------------------------------------------------------
+// k-steps [k0/64, k0/64 + nk).
+template <int BM, int BN, int FM, int FN, bool SW>
+__device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
+                                              uint16_t* lds, int tid, int a_base, int b_base,
+                                              const int* xo, f32x16_t (&acc)[FM][FN]) {
+  using LA = LoaderMNMajor<BM>;
+  using LB = LoaderMNMajor<BN>;
+  constexpr int SA = BM * kBK, STAGE = (BM + BN) * kBK;
+  LA a0, a1;
+  LB b0, b1;
+  a0.init_interior(p.lda, tid);
+  a1.init_interior(p.lda, tid);
+  b0.init_interior(p.ldb, tid);
+  b1.init_interior(p.ldb, tid);
+  // k-steps past the end re-read k-step 0 (never stored), keeping the loads
+  // of every k-step alike
+  auto kof = [nk](int t) { return (t < nk ? t : 0) * kBK; };
+  auto load = [&](LA& a, LB& b, int t) __attribute__((always_inline)) {
+    a.load_interior(p.A, p.lda, m0, k0 + kof(t));
+    b.load_interior(p.B, p.ldb, n0, k0 + kof(t));
+  };
+  // the sets for k-steps 0 / 2 and 1: with nk odd k-step 0 runs before the
+  // loop on (a0, b0), so the roles swap (see mix_mainloop)
+  const bool odd = nk & 1;
+  if (odd) {
+    load(a1, b1, 0);
+    load(a0, b0, 1);
+    a1.store(lds, tid);
+    b1.store(lds + SA, tid);
+    load(a1, b1, 2);
+  } else {
+    load(a0, b0, 0);
+    load(a1, b1, 1);
+    a0.store(lds, tid);
+    b0.store(lds + SA, tid);
+    load(a0, b0, 2);
+  }
+  __syncthreads();
+  bf16x8_t fa[2][FM], fb[2][FN];
+  read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+  // k-step kt; (a, b) hold k-step kt+1 and then receive kt+3
+  auto step = [&](LA& a, LB& b, int kt) __attribute__((always_inline)) {
+    const int cur = kt & 1;
+    const bool more = kt + 1 < nk;
+    const uint16_t* st = lds + cur * STAGE;
+    uint16_t* nx = lds + (cur ^ 1) * STAGE;
+    __builtin_amdgcn_sched_barrier(0);
+    plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[1]);
+    plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
+    store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3], a, b,
+                               nx, nx + SA, tid, more);
+    __syncthreads();
+    load(a, b, kt + 3);
+    // (in the last k-step this reads a stale stage that is never used)
+    plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
+  };
+  // two unconditional steps per iteration (see mix_mainloop)
+  int kt0 = 0;
+  if (odd) {
+    step(a0, b0, 0);
+    kt0 = 1;
+  }
+  for (int kt = kt0; kt < nk; kt += 2) {
+    step(a1, b1, kt);
+    step(a0, b0, kt + 1);
+  }
+  // the trailing loads must land before the registers are reused
+  wait_dma();
 }
 
 // ----------------------------------------------------------------------
@@ -1300,6 +1401,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr bool GA = EPI == kEpiGStoreBf16 || EPI == kEpiGStoreF32;  // CE gradient A on load
   // one K-contiguous operand, 256x256: the mixed loop (three D + two G panels)
   constexpr bool MIX = TGEMM_MIX && (A_KMAJOR != B_KMAJOR) && BM == 256 && BN == 256 && !Q8 && !GA;
+  // neither operand K-contiguous, 256x256: two register sets per operand
+  constexpr bool REG2 = TGEMM_MIX && !A_KMAJOR && !B_KMAJOR && BM == 256 && BN == 256 && !Q8 && !GA;
   constexpr int LDS_ELEMS =
       MIX ? 2 * SA + 3 * SB
           : ((A_KMAJOR && B_KMAJOR && !Q8 && !GA && RING > 2 * STAGE) ? RING : 2 * STAGE);
@@ -1352,18 +1455,25 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
     }
   }
   if constexpr (MIX) {
-    if (interior && ((kend - kbeg) / kBK) % 2 == 0) {
-      mix_mainloop<BM, BN, FM, FN, A_KMAJOR, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, tid,
-                                                 wave, lane, a_base, b_base - SA, xo, acc);
+    if (interior) {
+      mix_mainloop<BM, BN, FM, FN, A_KMAJOR, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds,
+                                                 lds + 3 * SA, tid, wave, lane, a_base,
+                                                 b_base - SA, xo, acc);
+      staged = true;
+    }
+  }
+  if constexpr (REG2) {
+    if (interior) {
+      reg2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, tid, a_base,
+                                        b_base, xo, acc);
       staged = true;
     }
   }
   // (both operands K-contiguous without the cast: interior tiles always take
   // a direct-copy loop above, so this path is not compiled for them)
-  // (with the mixed loop compiled, an interior tile with an odd k-step count
-  // takes the general path: a third main loop merging its accumulators into
-  // the epilogue makes the register allocator spill there)
-  constexpr bool kRegInterior = (!(A_KMAJOR && B_KMAJOR) || Q8 || GA) && !MIX;
+  // (not compiled with the mixed or two-set loop: a third main loop merging
+  // its accumulators into the epilogue makes the register allocator spill)
+  constexpr bool kRegInterior = (!(A_KMAJOR && B_KMAJOR) || Q8 || GA) && !MIX && !REG2;
   if (kRegInterior && !staged && interior) {
     // Register path, interior tiles: one buffer load per 16-byte vector and
     // no bounds tests.  The loads of k-step kt+1 are issued right after the
@@ -1489,7 +1599,8 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
 
   __syncthreads();  // every wave is done with LDS (the CE epilogue reuses it)
-  if constexpr (EPI == kEpiStoreBf16 || EPI == kEpiStoreF32) {
+  // (split products always launch the fp32 store instance)
+  if constexpr (EPI == kEpiStoreF32) {
     if (p.splitk > 1) {
       // K chunk ks of a split product: its fp32 partial goes to slice ks of
       // the workspace; a second kernel adds the slices in chunk order.

@@ -60,6 +60,22 @@ def test_integer_valued_is_exact(M, N, K, ta, tb):
     assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("ta,tb", LAYOUTS)
+@pytest.mark.parametrize("K", [320, 384, 64, 4096 - 64])
+def test_interior_256_tiles_odd_and_even_k_steps(K, ta, tb):
+    """Whole 256x256 tiles in every layout with an odd (5, 1, 63) and an
+    even (6) count of 64-wide k-steps: the direct-copy, mixed and two-set
+    loops peel k-step 0 when the count is odd.  Integer entries: the
+    oracle's bits, in fp32 and bf16 output."""
+    M, N = 512, 768
+    d = workloads.random_operands(M, N, K, ta, tb, seed=K + 5, int_range=3)
+    ref = oracle_gemm_from(d, ta, tb, M, N, K)
+    C = run_store(d, ta, tb, M, N, K, out_dtype=torch.float32, cfg=1)
+    assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
+    Cb = run_store(d, ta, tb, M, N, K, cfg=1)
+    assert np.array_equal(bits(Cb), oracle.f64_to_bf16_bits(ref))
+
+
 def test_integer_valued_bf16_output_is_exact():
     # |C| <= 256 keeps every integer exactly representable in bf16
     M, N, K = 200, 136, 16
