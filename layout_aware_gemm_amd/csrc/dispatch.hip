@@ -616,11 +616,10 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
         launch_gemm(transA, transB, cfg, bf16_out ? kEpiQ8Bf16 : kEpiQ8F32, p, s));
   uint8_t* qa = static_cast<uint8_t*>(w.ptr);
   uint8_t* qb = static_cast<uint8_t*>(w.ptr) + offB;
-  hipError_t e = launch_q8_pack(p.A, lda, is_n(transA), (int)M, (int)K, scales, qa, (int)Mp,
-                                (int)Kp, s);
-  if (e == hipSuccess)
-    e = launch_q8_pack(p.B, ldb, !is_n(transB), (int)N, (int)K, scales + 1, qb, (int)Np, (int)Kp,
-                       s);
+  const PackOperand pa = {p.A, lda, is_n(transA), (int)M, (int)K, scales, qa, (int)Mp, (int)Kp};
+  const PackOperand pb = {p.B, ldb, !is_n(transB), (int)N, (int)K, scales + 1, qb, (int)Np,
+                          (int)Kp};
+  hipError_t e = launch_q8_pack(pa, pb, s);
   if (e == hipSuccess) {
     p.A = reinterpret_cast<const uint16_t*>(qa);
     p.B = reinterpret_cast<const uint16_t*>(qb);

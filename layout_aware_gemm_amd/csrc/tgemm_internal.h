@@ -126,12 +126,20 @@ hipError_t launch_k1_ce(const uint16_t* a, int64_t sa, const uint16_t* b, int64_
 
 // e4m3fn cast (scale[0], clamp, round) of an fp8 GEMM operand into the
 // K-contiguous code matrix out [Rp][Kp] (one byte per code, zero past R
-// rows and K columns) that launch_gemm_f8 reads (defined in fp8_cast.hip).
-// k_contiguous: X is [R][K] with row stride ld (K % 8 == 0); otherwise X is
-// [K][R] with row stride ld (R % 8 == 0).  X 16-byte aligned, ld % 8 == 0,
-// Rp % 64 == 0, Kp % 128 == 0.
-hipError_t launch_q8_pack(const uint16_t* X, int64_t ld, bool k_contiguous, int R, int K,
-                          const float* scale, uint8_t* out, int Rp, int Kp, hipStream_t s);
+// rows and K columns) that launch_gemm_f8 reads.  k_contiguous: X is [R][K]
+// with row stride ld (K % 8 == 0); otherwise X is [K][R] with row stride ld
+// (R % 8 == 0).  X 16-byte aligned, ld % 8 == 0, Rp % 64 == 0, Kp % 128 == 0.
+struct PackOperand {
+  const uint16_t* X;
+  int64_t ld;
+  bool k_contiguous;
+  int R, K;
+  const float* scale;
+  uint8_t* out;
+  int Rp, Kp;
+};
+// Both operands of one product in one launch (defined in fp8_cast.hip).
+hipError_t launch_q8_pack(const PackOperand& a, const PackOperand& b, hipStream_t s);
 
 // fp8 matrix-core GEMM over two packed code matrices (defined in
 // gemm_f8.hip): p.A [tilesM*BM][2*p.K] and p.B [tilesN*BN][2*p.K] bytes
