@@ -595,17 +595,40 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
   const bool bf16_out = epilogue == TGEMM_EPI_STORE_BF16;
   // the stored rows' lengths (the contiguous axis)
   const int64_t colsA = is_n(transA) ? K : M, colsB = is_n(transB) ? N : K;
-  const int BT = tile_rows(cfg);
-  const int64_t Mp = (int64_t)ceil_div(M, BT) * BT, Np = (int64_t)ceil_div(N, BT) * BT;
+  // fp8 tile: the shape whose grid fills the chip best, by an estimate of
+  // time = waves of 256 tiles x tile area / the shape's relative rate per
+  // compute unit (measured on the fp8 kernel: 256x192 0.9 of 256x256,
+  // 128x128 about 0.56).  At 4096x3072 the 256x192 tile gives exactly 256
+  // tiles where 256x256 leaves 64 compute units idle.
+  int f8t = kF8Tile256x256;
+  if (g_forced_tile == kTile128) {
+    f8t = kF8Tile128x128;
+  } else if (g_forced_tile == kTileAuto) {
+    double best = 0.0;
+    const int cand[3] = {kF8Tile256x256, kF8Tile256x192, kF8Tile128x128};
+    const double rate[3] = {1.0, 0.9, 0.56};
+    for (int c = 0; c < 3; ++c) {
+      const int64_t tiles =
+          (int64_t)ceil_div(M, f8_tile_rows(cand[c])) * ceil_div(N, f8_tile_cols(cand[c]));
+      const double t = (double)((tiles + 255) / 256) * f8_tile_rows(cand[c]) *
+                       f8_tile_cols(cand[c]) / rate[c];
+      if (c == 0 || t < best) {
+        best = t;
+        f8t = cand[c];
+      }
+    }
+  }
+  const int BTM = f8_tile_rows(f8t), BTN = f8_tile_cols(f8t);
+  const int64_t Mp = (int64_t)ceil_div(M, BTM) * BTM, Np = (int64_t)ceil_div(N, BTN) * BTN;
   const int64_t Kp = (K + 127) / 128 * 128;
   const bool packed = g_fp8_cast_once && p.aligned && colsA % 8 == 0 && colsB % 8 == 0 &&
                       ceil_div(M, 256) >= 2 && ceil_div(N, 256) >= 2 && Kp / 2 < (1 << 23);
   if (verbose())
     fprintf(stderr,
             "tgemm: fp8 gemm %c%c M=%lld N=%lld K=%lld tile=%d grid=%dx%d aligned=%d "
-            "packed=%d\n",
+            "packed=%d (%dx%d tiles)\n",
             transA, transB, (long long)M, (long long)N, (long long)K, cfg, p.tilesM, p.tilesN,
-            p.aligned, packed ? 1 : 0);
+            p.aligned, packed ? 1 : 0, BTM, BTN);
   // the two code matrices, B's at a 256-byte boundary; without the memory
   // for them the product casts on load instead
   const size_t bytesA = (size_t)Mp * (size_t)Kp;
@@ -626,9 +649,10 @@ extern "C" int tgemm_run_fp8(char transA, char transB, int64_t M, int64_t N, int
     p.lda = p.ldb = Kp / 2;
     p.K = (int)(Kp / 2);
     p.kchunk = p.K;
-    p.tilesM = (int)(Mp / BT);
-    p.tilesN = (int)(Np / BT);
-    e = launch_gemm_f8(cfg, bf16_out ? kEpiOsBf16 : kEpiOsF32, p, s);
+    p.tilesM = (int)(Mp / BTM);
+    p.tilesN = (int)(Np / BTN);
+    p.groupM = p.tilesM < 4 ? p.tilesM : (p.tilesM <= 8 ? p.tilesM : 4);
+    e = launch_gemm_f8(f8t, bf16_out ? kEpiOsBf16 : kEpiOsF32, p, s);
   }
   const hipError_t r = release_workspace(w, s);
   return status_of(e != hipSuccess ? e : r);

@@ -50,8 +50,9 @@ struct Frag8 {
 
 // One 64-k substep: MFMA q with `cur`; the half-fragment reads of the next
 // substep (chunks at element offsets x0, x1 of the rows at pa / pb) into
-// `nxt`, spread evenly over the slots; and, when `cp` is set, this wave's
-// copies of one panel (d, origin o, into dst), one every STEP slots.
+// `nxt`; and, when `cp` is set, this wave's copies of one panel (d, origin
+// o, into dst).  Item i of n side items goes with slot floor(i * SL / n),
+// so they spread evenly over the slots whatever their count.
 template <int FM, int FN, int R>
 __device__ __forceinline__ void f8_substep(f32x16_t (&acc)[FM][FN], const Frag8<FM, FN>& cur,
                                            Frag8<FM, FN>& nxt, const uint16_t* pa,
@@ -60,15 +61,13 @@ __device__ __forceinline__ void f8_substep(f32x16_t (&acc)[FM][FN], const Frag8<
                                            uint16_t* dst, int wave_u) {
   constexpr int SL = FM * FN, RD = 2 * (FM + FN);
   constexpr int NCP = DmaPanel<R>::PER_WAVE;
-  constexpr int STEP = SL / NCP;
-  static_assert(STEP * NCP == SL, "copies must divide the slots evenly");
-  static_assert(RD % SL == 0, "reads must divide the slots evenly");
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
     const int i = q / FN, j = q % FN;
     acc[i][j] = mma_f8(cur.a[i][0], cur.a[i][1], cur.b[j][0], cur.b[j][1], acc[i][j]);
 #pragma unroll
-    for (int r = q * (RD / SL); r < (q + 1) * (RD / SL); ++r) {
+    for (int r = 0; r < RD; ++r) {
+      if ((r * SL) / RD != q) continue;
       const int f = r >> 1, hf = r & 1;
       const int x = hf ? x1 : x0;
       if (f < FM)
@@ -76,7 +75,11 @@ __device__ __forceinline__ void f8_substep(f32x16_t (&acc)[FM][FN], const Frag8<
       else
         nxt.b[f - FM][hf] = *reinterpret_cast<const i32x4_t*>(pb + (f - FM) * 32 * kBK + x);
     }
-    if (cp && q % STEP == 0) d.issue_one(o, dst, wave_u, q / STEP);
+    if (cp) {
+#pragma unroll
+      for (int c = 0; c < NCP; ++c)
+        if ((c * SL) / NCP == q) d.issue_one(o, dst, wave_u, c);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -92,7 +95,6 @@ __device__ __forceinline__ void f8_mainloop(const GemmParams& p, int m0, int n0,
                                             f32x16_t (&acc)[FM][FN]) {
   constexpr int SA = BM * kBK, SB = BN * kBK;
   constexpr int NA = DmaPanel<BM>::PER_WAVE, NB = DmaPanel<BN>::PER_WAVE;
-  static_assert(NA == NB, "one wait count for both operands");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   DmaPanel<BM> da;
   DmaPanel<BN> db;
@@ -154,9 +156,8 @@ __device__ __forceinline__ void f8_mainloop(const GemmParams& p, int m0, int n0,
 // p.A, p.B: the packed code matrices as 16-bit units (p.lda = p.ldb = Kp/2,
 // p.K = Kp/2); p.tilesM x p.tilesN tiles cover them exactly; p.M, p.N are
 // the output's extent (the epilogue stores only those).
-template <int BM, int EPI>
+template <int BM, int BN, int EPI>
 __global__ void __launch_bounds__(kThreads, 1) gemm_f8_kernel(GemmParams p) {
-  constexpr int BN = BM;
   constexpr int WM = BM / 2, WN = BN / 2;
   constexpr int FM = WM / 32, FN = WN / 32;
   constexpr int SA = BM * kBK, SB = BN * kBK;
@@ -187,22 +188,26 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_f8_kernel(GemmParams p) {
   epilogue<EPI, FM, FN, BM, kThreads>(p, acc, m0, n0, wm * WM, wn * WN, 0, lds, tid, lane);
 }
 
-template <int BM>
+template <int BM, int BN>
 hipError_t launch_f8_tpl(int epi, const GemmParams& p, hipStream_t s) {
   const dim3 grid(p.tilesM * p.tilesN), block(kThreads);
   if (epi == kEpiOsBf16)
-    hipLaunchKernelGGL((gemm_f8_kernel<BM, kEpiOsBf16>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_f8_kernel<BM, BN, kEpiOsBf16>), grid, block, 0, s, p);
   else
-    hipLaunchKernelGGL((gemm_f8_kernel<BM, kEpiOsF32>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((gemm_f8_kernel<BM, BN, kEpiOsF32>), grid, block, 0, s, p);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_gemm_f8(int cfg, int epi, const GemmParams& p, hipStream_t s) {
+hipError_t launch_gemm_f8(int tile, int epi, const GemmParams& p, hipStream_t s) {
   if (epi != kEpiOsBf16 && epi != kEpiOsF32) return hipErrorInvalidValue;
-  if (cfg == kTile256) return launch_f8_tpl<256>(epi, p, s);
-  return launch_f8_tpl<128>(epi, p, s);
+  switch (tile) {
+    case kF8Tile256x256: return launch_f8_tpl<256, 256>(epi, p, s);
+    case kF8Tile256x192: return launch_f8_tpl<256, 192>(epi, p, s);
+    case kF8Tile128x128: return launch_f8_tpl<128, 128>(epi, p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace tgemm

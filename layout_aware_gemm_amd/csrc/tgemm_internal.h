@@ -144,7 +144,10 @@ hipError_t launch_q8_pack(const PackOperand& a, const PackOperand& b, hipStream_
 // fp8 matrix-core GEMM over two packed code matrices (defined in
 // gemm_f8.hip): p.A [tilesM*BM][2*p.K] and p.B [tilesN*BN][2*p.K] bytes
 // passed as 16-bit units (p.lda = p.ldb = p.K, p.K % 64 == 0), an OS
-// epilogue, C [p.M][p.N].  cfg: kTile256 or kTile128.
-hipError_t launch_gemm_f8(int cfg, int epi, const GemmParams& p, hipStream_t s);
+// epilogue, C [p.M][p.N].  tile: one of the F8Tile shapes (BM x BN).
+enum F8Tile : int { kF8Tile256x256 = 0, kF8Tile256x192 = 1, kF8Tile128x128 = 2 };
+inline int f8_tile_rows(int t) { return t == kF8Tile128x128 ? 128 : 256; }
+inline int f8_tile_cols(int t) { return t == kF8Tile256x256 ? 256 : t == kF8Tile256x192 ? 192 : 128; }
+hipError_t launch_gemm_f8(int tile, int epi, const GemmParams& p, hipStream_t s);
 
 }  // namespace tgemm

@@ -198,11 +198,12 @@ def test_cast_once_keeps_nan():
         assert np.all(np.abs(got - ref)[ok] <= bound[ok])
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [0, 1, 2])
 def test_layouts_and_tiles_give_the_same_bits(cfg):
     """The cast happens before the (layout-independent) image the matrix
-    cores read -- the packed codes here -- so all four layouts, and both
-    tile configurations, give identical bits."""
+    cores read -- the packed codes here -- so all four layouts, and every
+    tile shape (256x256, 128x128, and the 256x192 the automatic choice
+    takes for this shape), give identical bits."""
     M, N, K = 384, 320, 448
     outs = []
     for ta, tb in LAYOUTS:
@@ -210,7 +211,7 @@ def test_layouts_and_tiles_give_the_same_bits(cfg):
         outs.append(run(d, ta, tb, M, N, K, (3.0, 7.0, 0.01), cfg=cfg))
     for o in outs[1:]:
         assert torch.equal(o, outs[0])
-    if cfg == 2:
+    if cfg != 1:
         d = workloads.random_operands(M, N, K, "N", "T", seed=12, std=20.0)
         assert torch.equal(run(d, "N", "T", M, N, K, (3.0, 7.0, 0.01), cfg=1), outs[0])
 
