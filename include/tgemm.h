@@ -331,8 +331,9 @@ TGEMM_API const char* tgemm_status_string(int status);
 /*
  * Tuning / testing knob: force the GEMM tile configuration for subsequent
  * calls from this process.  0 = automatic (default); 1 = 256x256 tiles;
- * 2 = 128x128 tiles.  Returns the previous value, or TGEMM_ERR_INVALID_ARG
- * for an unknown value.
+ * 2 = 128x128 tiles; 3 = 192x256 tiles for NT products with a store
+ * epilogue (256x256 for any other call).  Returns the previous value, or
+ * TGEMM_ERR_INVALID_ARG for an unknown value.
  * Not thread-safe with concurrent tgemm_run calls.
  */
 TGEMM_API int tgemm_set_tile_config(int config);

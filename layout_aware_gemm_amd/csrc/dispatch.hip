@@ -57,13 +57,23 @@ int choose_tile(bool nt, int M, int N, int K, int epilogue, int* split) {
   const bool store = epilogue == TGEMM_EPI_STORE_BF16 || epilogue == TGEMM_EPI_STORE_F32;
   int cfg, s = 1;
   if (g_forced_tile != kTileAuto) {
-    cfg = g_forced_tile;
+    // (192x256 tiles exist for NT store epilogues only)
+    cfg = g_forced_tile == kTile192 && !(nt && store) ? kTile256 : g_forced_tile;
   } else if (t256 >= 200) {
     cfg = kTile256;
   } else {
     const int64_t fill = 256 / t256, by_k = K / 2048;
     const int64_t auto_s = fill < by_k ? fill : by_k;
-    if (nt && store && auto_s >= 2) {
+    // 192x256 tiles when M is a multiple of 192 and they keep as many
+    // workgroups busy with fewer K chunks, so fewer fp32 partial products
+    // (768x5120: 80 tiles x 3 chunks against 60 x 4)
+    const int64_t t192 = (int64_t)ceil_div(M, 192) * ceil_div(N, 256);
+    const int64_t f192 = 256 / t192, s192 = f192 < by_k ? f192 : by_k;
+    if (nt && store && M % 192 == 0 && s192 >= 2 && t192 * s192 >= t256 * auto_s &&
+        s192 < auto_s) {
+      cfg = kTile192;
+      s = (int)s192;
+    } else if (nt && store && auto_s >= 2) {
       cfg = kTile256;
       s = (int)auto_s;
     } else {
@@ -242,7 +252,7 @@ extern "C" int tgemm_set_fp8_cast_once(int enable) {
 }
 
 extern "C" int tgemm_set_tile_config(int config) {
-  if (config < kTileAuto || config > kTile128) return TGEMM_ERR_INVALID_ARG;
+  if (config < kTileAuto || config > kTile192) return TGEMM_ERR_INVALID_ARG;
   const int prev = g_forced_tile;
   g_forced_tile = config;
   return prev;

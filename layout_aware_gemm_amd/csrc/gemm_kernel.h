@@ -1086,15 +1086,20 @@ __device__ __forceinline__ void copy_substep(f32x16_t (&acc)[FM][FN], const bf16
                                              const DmaPanel<R>& d, const uint16_t* o,
                                              uint16_t* dst, int wave_u) {
   constexpr int NCP = DmaPanel<R>::PER_WAVE;
-  constexpr int STEP = FM * FN / NCP;
-  static_assert(STEP * NCP == FM * FN, "copies must divide the slots evenly");
+  constexpr int SL = FM * FN;
 #pragma unroll
   for (int q = 0; q < FM * FN; ++q) {
     const int i = q / FN, j = q % FN;
     acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
-    if (cp && q % STEP == 0) d.issue_one(o, dst, wave_u, q / STEP);
+    // copy c goes with slot floor(c * SL / NCP): evenly spread whatever the
+    // counts (one every other slot for a 256x256 tile)
+    if (cp) {
+#pragma unroll
+      for (int c = 0; c < NCP; ++c)
+        if ((c * SL) / NCP == q) d.issue_one(o, dst, wave_u, c);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1108,7 +1113,6 @@ __device__ __forceinline__ void dma3_mainloop(const GemmParams& p, int m0, int n
                                               f32x16_t (&acc)[FM][FN]) {
   constexpr int SA = BM * kBK, SB = BN * kBK;
   constexpr int NA = DmaPanel<BM>::PER_WAVE, NB = DmaPanel<BN>::PER_WAVE;
-  static_assert(NA == NB, "one wait count for both operands");
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
   DmaPanel<BM> da;
   DmaPanel<BN> db;
@@ -1403,9 +1407,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr bool MIX = TGEMM_MIX && (A_KMAJOR != B_KMAJOR) && BM == 256 && BN == 256 && !Q8 && !GA;
   // neither operand K-contiguous, 256x256: two register sets per operand
   constexpr bool REG2 = TGEMM_MIX && !A_KMAJOR && !B_KMAJOR && BM == 256 && BN == 256 && !Q8 && !GA;
+  // (NT: the three-buffer loop for 256- and 192-row tiles, the ring for 128)
+  constexpr int DMA3 = 2 * SA + 3 * SB;
+  constexpr int NT_LDS = BM == 128 ? (RING > 2 * STAGE ? RING : 2 * STAGE)
+                                   : (DMA3 > 2 * STAGE ? DMA3 : 2 * STAGE);
   constexpr int LDS_ELEMS =
-      MIX ? 2 * SA + 3 * SB
-          : ((A_KMAJOR && B_KMAJOR && !Q8 && !GA && RING > 2 * STAGE) ? RING : 2 * STAGE);
+      MIX ? DMA3 : ((A_KMAJOR && B_KMAJOR && !Q8 && !GA) ? NT_LDS : 2 * STAGE);
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
 
   const int tid = threadIdx.x;
@@ -1443,15 +1450,20 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   bool staged = false;  // main loop done on a global->LDS copy path
   // (the direct copies move raw bf16, so Q8 operands take the register path)
   if constexpr (A_KMAJOR && B_KMAJOR && !Q8 && !GA) {
-    if (interior && BM == 256) {
-      static_assert(BM != 256 || 2 * SA + 3 * SB <= LDS_ELEMS, "three B panels must fit");
-      dma3_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
-                                        a_base, b_base - SA, xo, acc);
-      staged = true;
-    } else if (interior) {
-      ring_mainloop<BM, BN, FM, FN, A_KMAJOR, B_KMAJOR, SW>(p, m0, n0, kbeg, (kend - kbeg) / kRK,
-                                                            lds, wave, lane, wm, wn, acc);
-      staged = true;
+    if constexpr (BM != 128) {
+      static_assert(2 * SA + 3 * SB <= LDS_ELEMS, "three B panels must fit");
+      if (interior) {
+        dma3_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, wave, lane,
+                                          a_base, b_base - SA, xo, acc);
+        staged = true;
+      }
+    } else {
+      if (interior) {
+        ring_mainloop<BM, BN, FM, FN, A_KMAJOR, B_KMAJOR, SW>(p, m0, n0, kbeg,
+                                                              (kend - kbeg) / kRK, lds, wave, lane,
+                                                              wm, wn, acc);
+        staged = true;
+      }
     }
   }
   if constexpr (MIX) {
@@ -1648,9 +1660,29 @@ hipError_t launch_gemm_tpl(int epi, const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 192x256 tiles: the NT store instances only (split products whose M is a
+// multiple of 192; see choose_tile).
+template <bool AK, bool BK>
+hipError_t launch_gemm_192(int epi, const GemmParams& p, hipStream_t s) {
+  if constexpr (AK && BK) {
+    const dim3 grid(p.tilesM * p.tilesN * p.splitk), block(kThreads);
+    if (epi == kEpiStoreBf16)
+      hipLaunchKernelGGL((gemm_kernel<192, 256, true, true, kEpiStoreBf16>), grid, block, 0, s, p);
+    else if (epi == kEpiStoreF32)
+      hipLaunchKernelGGL((gemm_kernel<192, 256, true, true, kEpiStoreF32>), grid, block, 0, s, p);
+    else
+      return hipErrorInvalidValue;
+    return hipGetLastError();
+  } else {
+    (void)epi, (void)p, (void)s;
+    return hipErrorInvalidValue;
+  }
+}
+
 template <bool AK, bool BK>
 hipError_t launch_gemm_layout(int cfg, int epi, const GemmParams& p, hipStream_t s) {
   if (cfg == kTile256) return launch_gemm_tpl<256, 256, AK, BK>(epi, p, s);
+  if (cfg == kTile192) return launch_gemm_192<AK, BK>(epi, p, s);
   return launch_gemm_tpl<128, 128, AK, BK>(epi, p, s);
 }
 

@@ -26,9 +26,9 @@ enum EpiKind : int {
   kEpiGStoreF32 = 8
 };
 
-// Tile configurations of the GEMM kernel (k-step 64): BM x BN = 256x256 or
-// 128x128, 4 waves in a 2x2 grid.
-enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2 };
+// Tile configurations of the GEMM kernel (k-step 64), 4 waves in a 2x2
+// grid: BM x BN = 256x256, 128x128, or 192x256 (NT store epilogues only).
+enum TileCfg : int { kTileAuto = 0, kTile256 = 1, kTile128 = 2, kTile192 = 3 };
 
 struct GemmParams {
   const uint16_t* A;  // bf16 bits
@@ -61,7 +61,7 @@ struct GemmParams {
 
 // Width (in columns) of the per-row partial blocks the CE epilogue writes.
 inline int ce_block_cols(int cfg) { return cfg == kTile256 ? 128 : 64; }
-inline int tile_rows(int cfg) { return cfg == kTile128 ? 128 : 256; }
+inline int tile_rows(int cfg) { return cfg == kTile128 ? 128 : cfg == kTile192 ? 192 : 256; }
 inline int tile_cols(int cfg) { return cfg == kTile128 ? 128 : 256; }
 
 // One launcher per operand layout (defined in gemm_<layout>.hip).

@@ -95,8 +95,11 @@ def test_run_rejects_before_touching_the_gpu():
 def test_set_tile_config_roundtrip():
     prev = tgemm.set_tile_config(2)
     assert tgemm.set_tile_config(prev) == 2
-    with pytest.raises(tgemm.TgemmError):
-        tgemm.set_tile_config(3)    # the eight-wave configuration is gone
+    prev = tgemm.set_tile_config(3)    # 192x256 (NT store products)
+    assert tgemm.set_tile_config(prev) == 3
+    for bad in (4, -1):
+        with pytest.raises(tgemm.TgemmError):
+            tgemm.set_tile_config(bad)
 
 
 def test_set_split_k_roundtrip():

@@ -36,7 +36,7 @@ def run_store(d, ta, tb, M, N, K, out_dtype=torch.bfloat16, cfg=0, ldc=None):
     return C
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 @pytest.mark.parametrize("pad", [0, 3])
 @pytest.mark.parametrize("ta,tb", LAYOUTS)
 @pytest.mark.parametrize("M,N,K", RAGGED)
@@ -86,7 +86,7 @@ def test_integer_valued_bf16_output_is_exact():
     assert np.array_equal(bits(C), oracle.f64_to_bf16_bits(ref))
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 def test_layouts_bitwise_identical(cfg):
     M, N, K = 384, 320, 448
     outs = []
@@ -99,12 +99,12 @@ def test_layouts_bitwise_identical(cfg):
 
 @pytest.mark.parametrize("M,N,K", [(300, 260, 200), (512, 768, 640)])
 def test_tile_configs_agree(M, N, K):
-    # the 256x256 and 128x128 tile kernels (interior tiles on the
+    # the 256x256, 128x128 and 192x256 tile kernels (interior tiles on the
     # global->LDS path, edge tiles on the register path) must produce the
     # same bits
     d = workloads.random_operands(M, N, K, "N", "T", seed=13)
-    outs = [run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=c) for c in (1, 2)]
-    assert torch.equal(outs[0], outs[1])
+    outs = [run_store(d, "N", "T", M, N, K, out_dtype=torch.float32, cfg=c) for c in (1, 2, 3)]
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
 
 
 def _spread_rows(X, ld):
@@ -219,7 +219,7 @@ def test_k1_store_is_exact_outer_product(out):
             assert np.array_equal(C.cpu().numpy().astype(np.float64), ref)
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 @pytest.mark.parametrize("split", [2, 3, 4])
 @pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (300, 260, 1000), (512, 256, 2112)])
 def test_split_k(M, N, K, split, cfg):
@@ -276,7 +276,7 @@ def test_streams_do_not_share_workspace():
         assert torch.equal(C, serial[i % 2])
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 @pytest.mark.parametrize("M,N,K", [(384, 200, 512), (200, 384, 512), (320, 320, 448), (520, 264, 192)])
 def test_ragged_k64_layouts_bitwise(M, N, K, cfg):
     """Ragged shapes with K a multiple of 64 (interior tiles on the
@@ -294,7 +294,7 @@ def test_ragged_k64_layouts_bitwise(M, N, K, cfg):
         assert torch.equal(v, outs["TN"]), k
 
 
-@pytest.mark.parametrize("cfg", [1, 2])
+@pytest.mark.parametrize("cfg", [1, 2, 3])
 @pytest.mark.parametrize("split", [2, 3])
 @pytest.mark.parametrize("M,N,K", [(256, 512, 4096), (384, 200, 1536)])
 def test_split_k_all_layouts_bitwise(M, N, K, split, cfg):
