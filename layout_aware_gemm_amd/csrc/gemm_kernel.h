@@ -1275,7 +1275,6 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
     uint16_t* gc = gbuf + (kt & 1) * SP;
     uint16_t* dn = dbuf + d3n * SP;
     uint16_t* gn = gbuf + ((kt + 1) & 1) * SP;
-    const bool more = kt + 1 < nk;
     const uint16_t* pa = pa_of(dc, gc);
     const uint16_t* pb = pb_of(dc, gc);
     __builtin_amdgcn_sched_barrier(0);
@@ -1283,8 +1282,11 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
                                 od + kof(kt + 2), dbuf + d3p * SP, wave_u, false, g, gn, tid);
     mix_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], pa + xo[2], pb + xo[2], false,
                                 dp, od, dbuf, wave_u, false, g, gn, tid);
+    // (the set always holds a k-step -- past the end a re-read of k-step
+    // 0 -- so its stores need no test: in the last k-step they fill a stage
+    // that is never multiplied)
     mix_substep<FM, FN, BM, SW>(acc, fa[0], fb[0], fa[1], fb[1], pa + xo[3], pb + xo[3], false,
-                                dp, od, dbuf, wave_u, more, g, gn, tid);
+                                dp, od, dbuf, wave_u, true, g, gn, tid);
     // D(kt+1) landed (after its copies: G(kt+2)'s loads and D(kt+2)'s
     // copies), the G stores and this wave's fragment reads done; after the
     // barrier no wave reads D(kt) or G(kt) any more
@@ -1364,14 +1366,14 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
   // k-step kt; (a, b) hold k-step kt+1 and then receive kt+3
   auto step = [&](LA& a, LB& b, int kt) __attribute__((always_inline)) {
     const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
     const uint16_t* st = lds + cur * STAGE;
     uint16_t* nx = lds + (cur ^ 1) * STAGE;
     __builtin_amdgcn_sched_barrier(0);
     plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[1]);
     plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
+    // (unconditional stores, as in mix_mainloop)
     store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3], a, b,
-                               nx, nx + SA, tid, more);
+                               nx, nx + SA, tid, true);
     __syncthreads();
     load(a, b, kt + 3);
     // (in the last k-step this reads a stale stage that is never used)
