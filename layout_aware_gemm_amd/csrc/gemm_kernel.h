@@ -464,19 +464,6 @@ __device__ __forceinline__ void map_tile(int bid, int tilesM, int tilesN, int gr
   tile_coords(tile, tilesM, tilesN, groupM, tm, tn);
 }
 
-template <int N>
-__device__ __forceinline__ float xor_max(float v) {
-#pragma unroll
-  for (int o = 1; o < N; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-template <int N>
-__device__ __forceinline__ float xor_sum(float v) {
-#pragma unroll
-  for (int o = 1; o < N; o <<= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-
 // ----------------------------------------------------------------------
 // Direct global -> LDS panel copy (interior tiles of K-contiguous operands).
 //
@@ -881,6 +868,78 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
 // A wave owns rows m0+wr0 .. +32*FM and columns n0+wc0 .. +32*FN.
 // The caller guarantees no wave still reads LDS (the CE path reuses it).
 // ----------------------------------------------------------------------
+// Column offset of register r of accumulator block j from the lane's first
+// column, in the cross-entropy's transposed accumulators.
+__device__ __forceinline__ int ce_cofs(int j, int r) { return j * 32 + 8 * (r >> 2) + (r & 3); }
+
+// exp(y - m) as 2^((y - m) * log2 e) on the hardware exp2, which returns 0
+// where the result would be subnormal: such terms lie below 2^-126 of a
+// block sum that holds at least 1 (the max's own term).
+__device__ __forceinline__ float ce_exp(float y, float m) {
+  return __builtin_amdgcn_exp2f((y - m) * kLog2e);
+}
+
+// Cross-entropy of one row block of transposed accumulators (the 16*FN
+// columns of row `row` that this lane holds, register r of block j at
+// column cl + ce_cofs(j, r); the other half of the wave's columns of the
+// row sit in lane l^32): the block max and the block sum of exp(y - max)
+// into the partial tables, and the label logit if the label's column is
+// among them.  Returns the max the exponentials were taken against.
+// EDGE: some of the lane's columns lie at or past N (only in the last
+// column of tiles); they read as -inf, so that the max and the sum take no
+// term from them (exp of -inf is 0).
+template <bool EDGE, int FN>
+__device__ __forceinline__ float ce_row_block(const GemmParams& p, const f32x16_t (&acc)[FN],
+                                              int row, int label, int cl, int h, int64_t pbase) {
+  f32x16_t v[FN];
+  if constexpr (EDGE) {
+    // the empty asm makes the limit opaque per row block, so that the 16*FN
+    // compares are made here, each used once, and not hoisted and held
+    // across the row blocks
+    int lim = p.N - cl;
+    asm volatile("" : "+v"(lim));
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) v[j][r] = ce_cofs(j, r) < lim ? acc[j][r] : -INFINITY;
+  }
+  auto y = [&](int j, int r) {
+    if constexpr (EDGE) return v[j][r];
+    return acc[j][r];
+  };
+  float mx = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, y(j, r));
+  mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+  // a block with no column inside N: its sum is 0 (not exp(-inf + inf))
+  const float mref = mx == -INFINITY ? 0.f : mx;
+  float sum = 0.f;
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sum += ce_exp(y(j, r), mref);
+  sum += __shfl_xor(sum, 32, 64);
+  // the label's offset from the lane's first column; the lane holds it if
+  // it falls in one of the lane's 4-column groups (bit 2 clear)
+  const int c = label - cl;
+  const bool hit = c >= 0 && c < 32 * FN && (c & 4) == 0;
+  if (__builtin_amdgcn_ballot_w64(hit)) {  // most row blocks hold no label
+    float ylab = 0.f;
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) ylab = c == ce_cofs(j, r) ? acc[j][r] : ylab;
+    if (hit && row < p.M) p.ylabel[row] = ylab;
+  }
+  if (h == 0 && row < p.M) {
+    p.part_m[pbase + row] = mx;
+    p.part_s[pbase + row] = sum;
+  }
+  return mref;
+}
+
 template <int EPI, int FM, int FN, int BM, int NTH, bool SW = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM][FN], int m0,
                                          int n0, int wr0, int wc0, int pcol, uint16_t* lds,
@@ -929,7 +988,8 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
             if (col0 + j * 32 < p.N) put(off + j * 32, acc[i][j][r]);
         }
     }
-  } else if constexpr (SW) {
+  } else {
+    static_assert(SW, "the cross-entropy epilogue reads transposed accumulators");
     // Cross-entropy on transposed accumulators: block (i,j), register r of
     // lane l holds C[row i*32 + l%32][col j*32 + 8*(r/4) + 4*(l/32) + r%4].
     // A lane owns 16*FN columns of one row; the other half of the wave's
@@ -945,118 +1005,48 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
     __syncthreads();
     const int64_t pbase = (int64_t)pcol * p.M;
     const bool vec8 = p.grad && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.grad) & 7) == 0;
+    // column of this lane's register 0 of block 0
+    const int cl = n0 + wc0 + 4 * h;
+    // the wave's columns reach past N only in the last column of tiles
+    const bool edge = __builtin_amdgcn_readfirstlane(n0 + wc0 + 32 * FN > p.N ? 1 : 0) != 0;
     float rmax[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
       const int lrow = wr0 + i * 32 + lc;
-      const int row = m0 + lrow;
-      const int lab = slab[lrow];
-      float mx = -INFINITY;
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = n0 + wc0 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          if (col < p.N) mx = fmaxf(mx, acc[i][j][r]);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      float sum = 0.f, ylab = 0.f;
-      bool hit = false;
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int col = n0 + wc0 + j * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-          const float y = acc[i][j][r];
-          const float e = exp2f((y - mx) * kLog2e);
-          sum += col < p.N ? e : 0.f;
-          hit = hit || (col == lab);
-          ylab = (col == lab) ? y : ylab;
-        }
-      sum += __shfl_xor(sum, 32, 64);
-      if (hit && row < p.M) p.ylabel[row] = ylab;
-      if (h == 0 && row < p.M) {
-        p.part_m[pbase + row] = mx;
-        p.part_s[pbase + row] = sum;
-      }
-      rmax[i] = mx;
+      if (edge)
+        rmax[i] = ce_row_block<true>(p, acc[i], m0 + lrow, slab[lrow], cl, h, pbase);
+      else
+        rmax[i] = ce_row_block<false>(p, acc[i], m0 + lrow, slab[lrow], cl, h, pbase);
       // one row block at a time: keeps only its 16*FN values live
       __builtin_amdgcn_sched_barrier(0);
     }
     if (p.grad) {
       // exp(y - block max) into the gradient buffer, 4 consecutive columns
-      // per 8-byte store (a separate pass, so the stores do not lengthen
-      // the live ranges of the reductions above)
+      // per 8-byte store (a pass of its own, so that the stores do not
+      // lengthen the live ranges of the reductions above)
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
         const int row = m0 + wr0 + i * 32 + lc;
         if (row >= p.M) continue;
+        uint16_t* grow = p.grad + (int64_t)row * p.ldc + cl;
 #pragma unroll
         for (int j = 0; j < FN; ++j)
 #pragma unroll
           for (int a = 0; a < 4; ++a) {
-            const int col0 = n0 + wc0 + j * 32 + 8 * a + 4 * h;
+            const int co = ce_cofs(j, 4 * a);
             float e[4];
 #pragma unroll
-            for (int b = 0; b < 4; ++b) e[b] = exp2f((acc[i][j][4 * a + b] - rmax[i]) * kLog2e);
-            uint16_t* g = p.grad + (int64_t)row * p.ldc + col0;
-            if (vec8 && col0 + 4 <= p.N) {
-              const uint32_t lo = pack_bf16x2(e[0], e[1]);
-              const uint32_t hi = pack_bf16x2(e[2], e[3]);
-              *reinterpret_cast<uint2*>(g) = make_uint2(lo, hi);
+            for (int b = 0; b < 4; ++b)
+              e[b] = ce_exp(acc[i][j][4 * a + b], rmax[i]);
+            if (vec8 && cl + co + 4 <= p.N) {
+              *reinterpret_cast<uint2*>(grow + co) =
+                  make_uint2(pack_bf16x2(e[0], e[1]), pack_bf16x2(e[2], e[3]));
             } else {
 #pragma unroll
               for (int b = 0; b < 4; ++b)
-                if (col0 + b < p.N) g[b] = to_bf16(e[b]);
+                if (cl + co + b < p.N) grow[co + b] = to_bf16(e[b]);
             }
           }
-      }
-    }
-  } else {
-    // Cross-entropy.  Per row of this wave's (32*FN)-column block: block
-    // max, block sum of exp(y - max), the label logit if the label column
-    // falls in the block, and optionally exp(y - block max) into the
-    // gradient buffer.  The logits themselves are not stored.
-    int* slab = reinterpret_cast<int*>(lds);
-    for (int t = tid; t < BM; t += NTH) {
-      const int row = m0 + t;
-      slab[t] = row < p.M ? p.labels[row] : -1;
-    }
-    __syncthreads();
-    const int64_t pbase = (int64_t)pcol * p.M;
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lrow = wr0 + i * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
-        const int row = m0 + lrow;
-        const int lab = slab[lrow];
-        float mx = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wc0 + j * 32 + lc;
-          if (col < p.N) mx = fmaxf(mx, acc[i][j][r]);
-        }
-        mx = xor_max<32>(mx);
-        float sum = 0.f, ylab = 0.f;
-        bool hit = false;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int col = n0 + wc0 + j * 32 + lc;
-          const float y = acc[i][j][r];
-          const float e = exp2f((y - mx) * kLog2e);
-          const bool ok = col < p.N;
-          sum += ok ? e : 0.f;
-          hit = hit || (col == lab);
-          ylab = (col == lab) ? y : ylab;
-          if (p.grad && ok && row < p.M) p.grad[(int64_t)row * p.ldc + col] = to_bf16(e);
-        }
-        if (hit && row < p.M) p.ylabel[row] = ylab;
-        sum = xor_sum<32>(sum);
-        if (lc == r && row < p.M) {
-          p.part_m[pbase + row] = mx;
-          p.part_s[pbase + row] = sum;
-        }
       }
     }
   }
