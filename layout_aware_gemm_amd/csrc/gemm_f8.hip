@@ -185,7 +185,7 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_f8_kernel(GemmParams p) {
 #pragma unroll
   for (int s = 0; s < 4; ++s) xo[s] = ((2 * s + h) ^ swz(lc)) << 3;
   f8_mainloop<BM, BN, FM, FN>(p, m0, n0, p.K / kBK, lds, wave, lane, a_base, b_local, xo, acc);
-  epilogue<EPI, FM, FN, BM, kThreads>(p, acc, m0, n0, wm * WM, wn * WN, 0, lds, tid, lane);
+  epilogue<EPI, FM, FN>(p, acc, m0, n0, wm * WM, wn * WN, 0, lane);
 }
 
 template <int BM, int BN>

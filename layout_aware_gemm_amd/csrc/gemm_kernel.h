@@ -866,7 +866,7 @@ __device__ __forceinline__ void ring_mainloop(const GemmParams& p, int m0, int n
 // Epilogues.  Accumulator layout of v_mfma_f32_32x32x16: lane l, register r
 // holds row 8*(r/4) + 4*(l/32) + r%4 and column l%32 of its 32x32 block.
 // A wave owns rows m0+wr0 .. +32*FM and columns n0+wc0 .. +32*FN.
-// The caller guarantees no wave still reads LDS (the CE path reuses it).
+// No epilogue touches LDS.
 // ----------------------------------------------------------------------
 // Column offset of register r of accumulator block j from the lane's first
 // column, in the cross-entropy's transposed accumulators.
@@ -940,10 +940,9 @@ __device__ __forceinline__ float ce_row_block(const GemmParams& p, const f32x16_
   return mref;
 }
 
-template <int EPI, int FM, int FN, int BM, int NTH, bool SW = false>
+template <int EPI, int FM, int FN, bool SW = false>
 __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM][FN], int m0,
-                                         int n0, int wr0, int wc0, int pcol, uint16_t* lds,
-                                         int tid, int lane) {
+                                         int n0, int wr0, int wc0, int pcol, int lane) {
   const int h = lane >> 5, lc = lane & 31;
   // (Q8, OS: the sum times the output scale, one fp32 multiply)
   constexpr bool OS = EPI == kEpiQ8Bf16 || EPI == kEpiQ8F32 || EPI == kEpiOsBf16 ||
@@ -997,12 +996,6 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
     // of exp(y - max), the label logit if its column is in the block, and
     // optionally exp(y - block max) into the gradient buffer (4 consecutive
     // columns per 8-byte store).  The logits themselves are not stored.
-    int* slab = reinterpret_cast<int*>(lds);
-    for (int t = tid; t < BM; t += NTH) {
-      const int row = m0 + t;
-      slab[t] = row < p.M ? p.labels[row] : -1;
-    }
-    __syncthreads();
     const int64_t pbase = (int64_t)pcol * p.M;
     const bool vec8 = p.grad && (p.ldc & 3) == 0 && (reinterpret_cast<uintptr_t>(p.grad) & 7) == 0;
     // column of this lane's register 0 of block 0
@@ -1012,11 +1005,12 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
     float rmax[FM];
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-      const int lrow = wr0 + i * 32 + lc;
+      const int row = m0 + wr0 + i * 32 + lc;
+      const int label = row < p.M ? p.labels[row] : -1;  // (lanes l, l^32 share a row)
       if (edge)
-        rmax[i] = ce_row_block<true>(p, acc[i], m0 + lrow, slab[lrow], cl, h, pbase);
+        rmax[i] = ce_row_block<true>(p, acc[i], row, label, cl, h, pbase);
       else
-        rmax[i] = ce_row_block<false>(p, acc[i], m0 + lrow, slab[lrow], cl, h, pbase);
+        rmax[i] = ce_row_block<false>(p, acc[i], row, label, cl, h, pbase);
       // one row block at a time: keeps only its 16*FN values live
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -1611,13 +1605,11 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
       GemmParams q = p;
       q.C = p.ws + (int64_t)ks * p.M * p.N;
       q.ldc = p.N;
-      epilogue<kEpiStoreF32, FM, FN, BM, kThreads>(q, acc, m0, n0, wm * WM, wn * WN, 0, lds, tid,
-                                                   lane);
+      epilogue<kEpiStoreF32, FM, FN>(q, acc, m0, n0, wm * WM, wn * WN, 0, lane);
       return;
     }
   }
-  epilogue<EPI, FM, FN, BM, kThreads, SW>(p, acc, m0, n0, wm * WM, wn * WN, tn * 2 + wn, lds, tid,
-                                          lane);
+  epilogue<EPI, FM, FN, SW>(p, acc, m0, n0, wm * WM, wn * WN, tn * 2 + wn, lane);
 }
 
 // Host-side launch of one instantiation.
