@@ -15,11 +15,7 @@ namespace tgemm {
 namespace {
 
 // One thread: 8 consecutive columns of one row (two 16-byte loads per
-// chunk when the rows are 16-byte aligned).  The loads of up to four chunks
-// are issued together before their adds, so that a thread waits for one
-// memory latency per four chunks rather than one per chunk.
-constexpr int kSumBatch = 4;
-
+// chunk when the rows are 16-byte aligned).
 __global__ void __launch_bounds__(256) splitk_sum_kernel(const float* __restrict__ ws, int split,
                                                          int M, int N, void* __restrict__ C,
                                                          int64_t ldc, int out_f32, int vec_in,
@@ -34,22 +30,14 @@ __global__ void __launch_bounds__(256) splitk_sum_kernel(const float* __restrict
   const bool full = c0 + 8 <= N;
   float v[8];
   if (vec_in && full) {
-    for (int q0 = 0; q0 < split; q0 += kSumBatch) {
-      float4 t[kSumBatch][2];
-#pragma unroll
-      for (int u = 0; u < kSumBatch; ++u)
-        if (q0 + u < split) {
-          t[u][0] = *reinterpret_cast<const float4*>(src + (q0 + u) * slice);
-          t[u][1] = *reinterpret_cast<const float4*>(src + (q0 + u) * slice + 4);
-        }
-#pragma unroll
-      for (int u = 0; u < kSumBatch; ++u) {
-        if (q0 + u >= split) break;
-        const float x[8] = {t[u][0].x, t[u][0].y, t[u][0].z, t[u][0].w,
-                            t[u][1].x, t[u][1].y, t[u][1].z, t[u][1].w};
-#pragma unroll
-        for (int e = 0; e < 8; ++e) v[e] = q0 + u == 0 ? x[e] : v[e] + x[e];
-      }
+    float4 a = *reinterpret_cast<const float4*>(src);
+    float4 b = *reinterpret_cast<const float4*>(src + 4);
+    v[0] = a.x, v[1] = a.y, v[2] = a.z, v[3] = a.w, v[4] = b.x, v[5] = b.y, v[6] = b.z, v[7] = b.w;
+    for (int q = 1; q < split; ++q) {
+      a = *reinterpret_cast<const float4*>(src + q * slice);
+      b = *reinterpret_cast<const float4*>(src + q * slice + 4);
+      v[0] += a.x, v[1] += a.y, v[2] += a.z, v[3] += a.w;
+      v[4] += b.x, v[5] += b.y, v[6] += b.z, v[7] += b.w;
     }
   } else {
 #pragma unroll
