@@ -320,14 +320,16 @@ struct LoaderMNMajor {
     sstep = (uint32_t)(ld * 2);
   }
 
-  __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0) {
+  // zero (uniform): an empty buffer range, so the vectors read as 0.
+  __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0,
+                                                bool zero = false) {
 #if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rs =
-        panel_rsrc(X + (int64_t)k0 * ld + r0, (uint32_t)(((int64_t)(kBK - 1) * ld + R) * 2));
+    const __amdgpu_buffer_rsrc_t rs = panel_rsrc(
+        X + (int64_t)k0 * ld + r0, zero ? 0u : (uint32_t)(((int64_t)(kBK - 1) * ld + R) * 2));
 #pragma unroll
     for (int j = 0; j < L; ++j) v[j] = buf_load16(rs, voff, j * sstep);
 #else
-    (void)X, (void)ld, (void)r0, (void)k0;
+    (void)X, (void)ld, (void)r0, (void)k0, (void)zero;
 #endif
   }
 
@@ -506,9 +508,11 @@ struct DmaPanel {
   }
 
   // Copy 1 KB block j of this wave's share.  origin = &X[r0][k0] (row r0
-  // of the tile, k-step k0) and panel are wave-uniform.
+  // of the tile, k-step k0) and panel are wave-uniform.  zero (uniform):
+  // the buffer gets an empty range, so every lane reads 0 and the block
+  // fills with zeros.
   __device__ __forceinline__ void issue_one(const uint16_t* origin, uint16_t* panel, int wave_u,
-                                            int j) const {
+                                            int j, bool zero = false) const {
     const int blk = wave_u * PER_WAVE + j;
 #if defined(__HIP_DEVICE_COMPILE__)
     // (device pass only: the host pass cannot form the LDS address-space
@@ -518,8 +522,9 @@ struct DmaPanel {
     const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
     void* src = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
     // word 3 = 0x00020000: 32-bit data format, the raw-buffer setting
-    __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-        src, (short)0, (int)__builtin_amdgcn_readfirstlane(extent), 0x00020000);
+    const int range = (int)__builtin_amdgcn_readfirstlane(extent);
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(src, (short)0, zero ? 0 : range, 0x00020000);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
         rs, (__attribute__((address_space(3))) void*)(panel + blk * 512), 16, (int)e[j & 1],
         (int)__builtin_amdgcn_readfirstlane(j * row8_bytes), 0, 0);
@@ -528,10 +533,10 @@ struct DmaPanel {
 #endif
   }
 
-  __device__ __forceinline__ void issue(const uint16_t* origin, uint16_t* panel,
-                                        int wave_u) const {
+  __device__ __forceinline__ void issue(const uint16_t* origin, uint16_t* panel, int wave_u,
+                                        bool zero = false) const {
 #pragma unroll
-    for (int j = 0; j < PER_WAVE; ++j) issue_one(origin, panel, wave_u, j);
+    for (int j = 0; j < PER_WAVE; ++j) issue_one(origin, panel, wave_u, j, zero);
   }
 };
 
@@ -1175,7 +1180,7 @@ __device__ __forceinline__ void mix_substep(f32x16_t (&acc)[FM][FN], const bf16x
                                             const uint16_t* pa, const uint16_t* pb, bool cp,
                                             const DmaPanel<R>& d, const uint16_t* o,
                                             uint16_t* ddst, int wave_u, bool st, const LG& g,
-                                            uint16_t* gdst, int tid) {
+                                            uint16_t* gdst, int tid, bool zero = false) {
   constexpr int SL = FM * FN;
   constexpr int NCP = DmaPanel<R>::PER_WAVE;
   static_assert(SL % NCP == 0 && SL % LG::U == 0, "side work must divide the slots evenly");
@@ -1185,7 +1190,7 @@ __device__ __forceinline__ void mix_substep(f32x16_t (&acc)[FM][FN], const bf16x
     acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
-    if (cp && q % (SL / NCP) == 0) d.issue_one(o, ddst, wave_u, q / (SL / NCP));
+    if (cp && q % (SL / NCP) == 0) d.issue_one(o, ddst, wave_u, q / (SL / NCP), zero);
     if (st && q % (SL / LG::U) == 0) g.store_unit(gdst, tid, q / (SL / LG::U));
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -1215,31 +1220,42 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
   LG g0, g1;
   g0.init_interior(ldg, tid);
   g1.init_interior(ldg, tid);
-  // k-steps past the end re-read k-step 0 (never stored or multiplied), so
+  // The loop runs an even number of k-steps, nke: with nk odd, k-step nk
+  // is one of zeros (both operands' loads get an empty buffer range), which
+  // adds exactly nothing to the sums.  A loop entered only from this
+  // prologue and from its own back edge sees the loads in one order, so the
+  // wait the compiler places before each register set's LDS stores waits
+  // for that set alone, giving its loads seven substeps to arrive.  (An odd
+  // k-step run outside the loop either merged two orders at the loop's
+  // entry, whose wait then also covered the other set, or, after the loop,
+  // made the register allocator spill the accumulators.)
+  const int nke = nk + (nk & 1);
+  // k-steps past nke re-read k-step 0 (never stored or multiplied), so
   // every k-step issues the same loads and the wait counts stay fixed
   auto kof = [nk](int t) { return (t < nk ? t : 0) * kBK; };
+  auto zero = [nk, nke](int t) { return t == nk && nke != nk; };
   // fragment rows: A's panel base + a_base, B's + b_local
   auto pa_of = [&](uint16_t* d, uint16_t* g) { return (AK ? d : g) + a_base; };
   auto pb_of = [&](uint16_t* d, uint16_t* g) { return (AK ? g : d) + b_local; };
-  // The step of k-step kt takes the set holding kt+1: g1 for even kt when
-  // nk is even.  With nk odd, k-step 0 runs before the loop on g0, so the
-  // loop's steps still come in pairs (g1, g0) and the sets swap roles here.
-  const bool odd = nk & 1;
+  // The step of k-step kt takes the set holding kt+1: g1 for even kt, g0
+  // for odd.
   auto prologue = [&](LG& s0, LG& s1) __attribute__((always_inline)) {
-    // s0 carries k-step 0, then k-step 2; s1 carries k-step 1
+    // s0 carries k-step 0, then k-step 2; s1 carries k-step 1.  The loads
+    // leave in the loop's own order -- the set of k-step kt+1, then the
+    // copies of D(kt+1), then the set of kt+2 -- so that the wait the
+    // compiler places before each set's LDS stores, which must hold for
+    // both the entry and the back edge of the loop, waits for that set
+    // alone and not also for the other one.
     dp.issue(od + kof(0), dbuf, wave_u);
     s0.load_interior(XG, ldg, rg0, k0 + kof(0));
-    dp.issue(od + kof(1), dbuf + SP, wave_u);
-    s1.load_interior(XG, ldg, rg0, k0 + kof(1));
+    s1.load_interior(XG, ldg, rg0, k0 + kof(1), zero(1));
+    dp.issue(od + kof(1), dbuf + SP, wave_u, zero(1));
     s0.store(gbuf, tid);
-    s0.load_interior(XG, ldg, rg0, k0 + kof(2));
+    s0.load_interior(XG, ldg, rg0, k0 + kof(2), zero(2));
   };
-  if (odd)
-    prologue(g1, g0);
-  else
-    prologue(g0, g1);
-  // D(0) landed (issued first; the rest may be in flight: G(0) done, D(1),
-  // G(1), G(2)); the G(0) stores done; other waves: the barrier
+  prologue(g0, g1);
+  // D(0) landed (issued first; the rest may be in flight: G(0) done, G(1),
+  // D(1), G(2)); the G(0) stores done; other waves: the barrier
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(ND + 2 * LG::L, 0));
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
@@ -1263,7 +1279,8 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
     const uint16_t* pb = pb_of(dc, gc);
     __builtin_amdgcn_sched_barrier(0);
     mix_substep<FM, FN, BM, SW>(acc, fa[0], fb[0], fa[1], fb[1], pa + xo[1], pb + xo[1], true, dp,
-                                od + kof(kt + 2), dbuf + d3p * SP, wave_u, false, g, gn, tid);
+                                od + kof(kt + 2), dbuf + d3p * SP, wave_u, false, g, gn, tid,
+                                zero(kt + 2));
     mix_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], pa + xo[2], pb + xo[2], false,
                                 dp, od, dbuf, wave_u, false, g, gn, tid);
     // (the set always holds a k-step -- past the end a re-read of k-step
@@ -1277,7 +1294,7 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(LG::L + ND, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    g.load_interior(XG, ldg, rg0, k0 + kof(kt + 3));
+    g.load_interior(XG, ldg, rg0, k0 + kof(kt + 3), zero(kt + 3));
     mix_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], pa_of(dn, gn) + xo[0],
                                 pb_of(dn, gn) + xo[0], false, dp, od, dbuf, wave_u, false, g, gn,
                                 tid);
@@ -1285,12 +1302,7 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
   // the body is two unconditional steps (a conditional second step, or a
   // second exit, merges two versions of the accumulators inside the loop,
   // which the register allocator does not keep in place)
-  int kt0 = 0;
-  if (odd) {
-    step(g0, 0);
-    kt0 = 1;
-  }
-  for (int kt = kt0; kt < nk; kt += 2) {
+  for (int kt = 0; kt < nke; kt += 2) {
     step(g1, kt);
     step(g0, kt + 1);
   }
@@ -1321,29 +1333,24 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
   a1.init_interior(p.lda, tid);
   b0.init_interior(p.ldb, tid);
   b1.init_interior(p.ldb, tid);
-  // k-steps past the end re-read k-step 0 (never stored), keeping the loads
-  // of every k-step alike
+  // An even number of k-steps, nke, with k-step nk of zeros when nk is odd
+  // (see mix_mainloop: one order of loads at the loop's entry and back
+  // edge, so each set's stores wait for that set alone).  k-steps past nke
+  // re-read k-step 0 (never stored), keeping the loads of every k-step
+  // alike.
+  const int nke = nk + (nk & 1);
   auto kof = [nk](int t) { return (t < nk ? t : 0) * kBK; };
   auto load = [&](LA& a, LB& b, int t) __attribute__((always_inline)) {
-    a.load_interior(p.A, p.lda, m0, k0 + kof(t));
-    b.load_interior(p.B, p.ldb, n0, k0 + kof(t));
+    const bool zero = t == nk && nke != nk;
+    a.load_interior(p.A, p.lda, m0, k0 + kof(t), zero);
+    b.load_interior(p.B, p.ldb, n0, k0 + kof(t), zero);
   };
-  // the sets for k-steps 0 / 2 and 1: with nk odd k-step 0 runs before the
-  // loop on (a0, b0), so the roles swap (see mix_mainloop)
-  const bool odd = nk & 1;
-  if (odd) {
-    load(a1, b1, 0);
-    load(a0, b0, 1);
-    a1.store(lds, tid);
-    b1.store(lds + SA, tid);
-    load(a1, b1, 2);
-  } else {
-    load(a0, b0, 0);
-    load(a1, b1, 1);
-    a0.store(lds, tid);
-    b0.store(lds + SA, tid);
-    load(a0, b0, 2);
-  }
+  // the sets for k-steps 0 / 2 and 1
+  load(a0, b0, 0);
+  load(a1, b1, 1);
+  a0.store(lds, tid);
+  b0.store(lds + SA, tid);
+  load(a0, b0, 2);
   __syncthreads();
   bf16x8_t fa[2][FM], fb[2][FN];
   read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
@@ -1364,12 +1371,7 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
     plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
   };
   // two unconditional steps per iteration (see mix_mainloop)
-  int kt0 = 0;
-  if (odd) {
-    step(a0, b0, 0);
-    kt0 = 1;
-  }
-  for (int kt = kt0; kt < nk; kt += 2) {
+  for (int kt = 0; kt < nke; kt += 2) {
     step(a1, b1, kt);
     step(a0, b0, kt + 1);
   }
