@@ -323,13 +323,31 @@ struct LoaderMNMajor {
   // zero (uniform): an empty buffer range, so the vectors read as 0.
   __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0,
                                                 bool zero = false) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rs = panel_rsrc(
-        X + (int64_t)k0 * ld + r0, zero ? 0u : (uint32_t)(((int64_t)(kBK - 1) * ld + R) * 2));
+    prep_interior(X, ld, r0, k0, zero);
 #pragma unroll
-    for (int j = 0; j < L; ++j) v[j] = buf_load16(rs, voff, j * sstep);
+    for (int j = 0; j < L; ++j) load_unit(j);
+  }
+
+  // The same loads one vector at a time, so that a loop can spread them
+  // between matrix-core instructions: prep_interior makes the panel's
+  // buffer resource, load_unit(j) loads vector j.
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t rs;
+#endif
+  __device__ __forceinline__ void prep_interior(const uint16_t* X, int64_t ld, int r0, int k0,
+                                                bool zero = false) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    rs = panel_rsrc(X + (int64_t)k0 * ld + r0,
+                    zero ? 0u : (uint32_t)(((int64_t)(kBK - 1) * ld + R) * 2));
 #else
     (void)X, (void)ld, (void)r0, (void)k0, (void)zero;
+#endif
+  }
+  __device__ __forceinline__ void load_unit(int j) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    v[j] = buf_load16(rs, voff, j * sstep);
+#else
+    (void)j;
 #endif
   }
 
@@ -596,6 +614,36 @@ __device__ __forceinline__ void plain_substep(f32x16_t (&acc)[FM][FN], const bf1
     acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
     if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
+// One k-substep without copies whose slots also issue the loads of
+// loaders la then lb (buffer resources already made), spread evenly: the
+// register loops' loads of k-step kt+3, which issued all at once fill the
+// address queue and hold up the matrix-core issue.
+template <int FM, int FN, bool SW, typename LdA, typename LdB>
+__device__ __forceinline__ void load2_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                              const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                              const uint16_t* rd_stage, int a_base, int b_base,
+                                              int xo, LdA& la, LdB& lb) {
+  constexpr int SL = FM * FN, U = LdA::L + LdB::L;
+  const uint16_t* pa = rd_stage + a_base + xo;
+  const uint16_t* pb = rd_stage + b_base + xo;
+#pragma unroll
+  for (int q = 0; q < SL; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    // units u with floor(u * SL / U) == q
+#pragma unroll
+    for (int u = (q * U + SL - 1) / SL; u < U && (u * SL) / U == q; ++u) {
+      if (u < LdA::L)
+        la.load_unit(u);
+      else
+        lb.load_unit(u - LdA::L);
+    }
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1179,11 +1227,13 @@ __device__ __forceinline__ void mix_substep(f32x16_t (&acc)[FM][FN], const bf16x
                                             const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
                                             const uint16_t* pa, const uint16_t* pb, bool cp,
                                             const DmaPanel<R>& d, const uint16_t* o,
-                                            uint16_t* ddst, int wave_u, bool st, const LG& g,
-                                            uint16_t* gdst, int tid, bool zero = false) {
+                                            uint16_t* ddst, int wave_u, bool st, LG& g,
+                                            uint16_t* gdst, int tid, bool zero = false,
+                                            bool ld = false) {
   constexpr int SL = FM * FN;
   constexpr int NCP = DmaPanel<R>::PER_WAVE;
-  static_assert(SL % NCP == 0 && SL % LG::U == 0, "side work must divide the slots evenly");
+  static_assert(SL % NCP == 0 && SL % LG::U == 0 && SL % LG::L == 0,
+                "side work must divide the slots evenly");
 #pragma unroll
   for (int q = 0; q < SL; ++q) {
     const int i = q / FN, j = q % FN;
@@ -1192,6 +1242,7 @@ __device__ __forceinline__ void mix_substep(f32x16_t (&acc)[FM][FN], const bf16x
     else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
     if (cp && q % (SL / NCP) == 0) d.issue_one(o, ddst, wave_u, q / (SL / NCP), zero);
     if (st && q % (SL / LG::U) == 0) g.store_unit(gdst, tid, q / (SL / LG::U));
+    if (ld && q % (SL / LG::L) == 0) g.load_unit(q / (SL / LG::L));
     __builtin_amdgcn_sched_barrier(0);
   }
 }
@@ -1294,10 +1345,12 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(LG::L + ND, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    g.load_interior(XG, ldg, rg0, k0 + kof(kt + 3), zero(kt + 3));
+    // G(kt+3)'s loads, one every SL/L slots of this substep (issued all at
+    // once they fill the address queue and hold up the matrix-core issue)
+    g.prep_interior(XG, ldg, rg0, k0 + kof(kt + 3), zero(kt + 3));
     mix_substep<FM, FN, BM, SW>(acc, fa[1], fb[1], fa[0], fb[0], pa_of(dn, gn) + xo[0],
                                 pb_of(dn, gn) + xo[0], false, dp, od, dbuf, wave_u, false, g, gn,
-                                tid);
+                                tid, false, true);
   };
   // the body is two unconditional steps (a conditional second step, or a
   // second exit, merges two versions of the accumulators inside the loop,
@@ -1366,9 +1419,12 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
     store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3], a, b,
                                nx, nx + SA, tid, true);
     __syncthreads();
-    load(a, b, kt + 3);
+    // the loads of k-step kt+3, spread over this substep
+    const bool zero = kt + 3 == nk && nke != nk;
+    a.prep_interior(p.A, p.lda, m0, k0 + kof(kt + 3), zero);
+    b.prep_interior(p.B, p.ldb, n0, k0 + kof(kt + 3), zero);
     // (in the last k-step this reads a stale stage that is never used)
-    plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0]);
+    load2_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0], a, b);
   };
   // two unconditional steps per iteration (see mix_mainloop)
   for (int kt = 0; kt < nke; kt += 2) {
