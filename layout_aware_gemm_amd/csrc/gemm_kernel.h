@@ -287,9 +287,27 @@ struct LoaderMNMajor {
   static constexpr int KBN = kBK / L; // k-groups per k-step
   uint4 v[L];
 
+  // Thread -> (k-group, mn-chunk).  With 8 k-groups (256-row panels) lane
+  // pairs take consecutive mn-chunks, so a load instruction reads 32
+  // contiguous bytes per pair (the texture unit's address queue fills less
+  // than with each lane on its own k row), while the 8 lanes of an LDS
+  // write group still cover 4 k-groups x 2 chunk parities, 8 distinct
+  // swizzled chunks: bit 0 of the thread is the chunk's low bit, bits 1-3
+  // the k-group, the rest the chunk's high bits.  Otherwise the k-group
+  // varies fastest.
+  static_assert(KBN != 8 || NTH == 256, "the paired mapping covers 8 k-groups x 32 chunks");
+  static __device__ __forceinline__ int kb_of(int tid) {
+    if constexpr (KBN == 8) return (tid >> 1) & 7;
+    return tid % KBN;
+  }
+  static __device__ __forceinline__ int mc_of(int tid) {
+    if constexpr (KBN == 8) return (tid & 1) | ((tid >> 4) << 1);
+    return tid / KBN;
+  }
+
   __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int r0,
                                        int Rt, int k0, int K, bool aligned, int tid) {
-    const int kb = tid % KBN, mc = tid / KBN;
+    const int kb = kb_of(tid), mc = mc_of(tid);
     const int gr = r0 + mc * 8;
 #pragma unroll
     for (int j = 0; j < L; ++j) {
@@ -315,7 +333,7 @@ struct LoaderMNMajor {
   uint32_t voff, sstep;
 
   __device__ __forceinline__ void init_interior(int64_t ld, int tid) {
-    const int kb = tid % KBN, mc = tid / KBN;
+    const int kb = kb_of(tid), mc = mc_of(tid);
     voff = (uint32_t)(((int64_t)kb * L * ld + mc * 8) * 2);
     sstep = (uint32_t)(ld * 2);
   }
@@ -361,7 +379,7 @@ struct LoaderMNMajor {
   float gs[L];
   int gl[L];
   __device__ __forceinline__ void load_g(const GemmParams& p, int r0, int k0, int tid) {
-    const int kb = tid % KBN, mc = tid / KBN;
+    const int kb = kb_of(tid), mc = mc_of(tid);
 #pragma unroll
     for (int j = 0; j < L; ++j) g_params(p, k0 + kb * L + j, r0 + mc * 8, gs[j], gl[j]);
   }
@@ -387,7 +405,7 @@ struct LoaderMNMajor {
   // between matrix-core instructions.
   static constexpr int U = 8;
   __device__ __forceinline__ void store_unit(uint16_t* lds, int tid, int i) const {
-    const int kb = tid % KBN, mc = tid / KBN;
+    const int kb = kb_of(tid), mc = mc_of(tid);
     const int row = mc * 8 + i;
     uint16_t* dst = lds + row * kBK;
     if constexpr (L == 8) {
@@ -410,7 +428,7 @@ struct LoaderMNMajor {
   }
 
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
-    const int kb = tid % KBN, mc = tid / KBN;
+    const int kb = kb_of(tid), mc = mc_of(tid);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int row = mc * 8 + i;
