@@ -275,36 +275,35 @@ struct LoaderKMajor {
 };
 
 // Operand contiguous along M/N: stored row k holds the m (or n) index.
-// Thread t owns k-group kb = t % KBN (L consecutive k) of mn-chunk
-// mc = t / KBN (8 consecutive rows of the panel); it loads L 16-byte vectors
-// (one per k) and transposes them.  The k-group varies fastest across lanes
-// so the transposed LDS writes of a lane group cover distinct chunks of one
-// row, while each global load instruction still covers whole 128-byte lines
-// (8 lanes with consecutive mc read 128 contiguous bytes of one k row).
+// Thread t owns k-group kb (L consecutive k) of mn-chunk mc (8 consecutive
+// rows of the panel); it loads L 16-byte vectors (one per k) and
+// transposes them into LDS rows.
 template <int R, int NTH = kThreads>
 struct LoaderMNMajor {
   static constexpr int L = R * 8 / NTH;  // k values per thread per k-step
   static constexpr int KBN = kBK / L; // k-groups per k-step
   uint4 v[L];
 
-  // Thread -> (k-group, mn-chunk).  With 8 k-groups (256-row panels) lane
-  // pairs take consecutive mn-chunks, so a load instruction reads 32
-  // contiguous bytes per pair (the texture unit's address queue fills less
-  // than with each lane on its own k row), while the 8 lanes of an LDS
-  // write group still cover 4 k-groups x 2 chunk parities, 8 distinct
-  // swizzled chunks: bit 0 of the thread is the chunk's low bit, bits 1-3
-  // the k-group, the rest the chunk's high bits.  Otherwise the k-group
-  // varies fastest.
-  static_assert(KBN != 8 || NTH == 256, "the paired mapping covers 8 k-groups x 32 chunks");
+  // Thread -> (k-group, mn-chunk).  A load instruction covers whole
+  // 128-byte lines either way; what differs is how many consecutive lanes
+  // read consecutive bytes.  With each lane on its own k row the loads
+  // crowded the texture unit's address queue, so with 8 k-groups (256-row
+  // panels) lane quads take consecutive mn-chunks and read 64 contiguous
+  // bytes: thread bits 0-1 are the chunk's low bits, bits 2-4 the k-group,
+  // the rest the chunk's high bits.  The cost is on the LDS side: the 8
+  // lanes of a write group then land on 4 distinct swizzled chunks, a
+  // two-way bank conflict, which measured cheaper than either reading 32
+  // bytes per lane pair without conflicts or selecting a per-lane row order
+  // that removes them.  Smaller panels: the k-group varies fastest.
+  static_assert(KBN != 8 || NTH == 256, "the quad mapping covers 8 k-groups x 32 chunks");
   static __device__ __forceinline__ int kb_of(int tid) {
-    if constexpr (KBN == 8) return (tid >> 1) & 7;
+    if constexpr (KBN == 8) return (tid >> 2) & 7;
     return tid % KBN;
   }
   static __device__ __forceinline__ int mc_of(int tid) {
-    if constexpr (KBN == 8) return (tid & 1) | ((tid >> 4) << 1);
+    if constexpr (KBN == 8) return (tid & 3) | ((tid >> 5) << 2);
     return tid / KBN;
   }
-
   __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int r0,
                                        int Rt, int k0, int K, bool aligned, int tid) {
     const int kb = kb_of(tid), mc = mc_of(tid);
