@@ -287,21 +287,24 @@ struct LoaderMNMajor {
   // Thread -> (k-group, mn-chunk).  A load instruction covers whole
   // 128-byte lines either way; what differs is how many consecutive lanes
   // read consecutive bytes.  With each lane on its own k row the loads
-  // crowded the texture unit's address queue, so with 8 k-groups (256-row
-  // panels) lane quads take consecutive mn-chunks and read 64 contiguous
-  // bytes: thread bits 0-1 are the chunk's low bits, bits 2-4 the k-group,
-  // the rest the chunk's high bits.  The cost is on the LDS side: the 8
-  // lanes of a write group then land on 4 distinct swizzled chunks, a
-  // two-way bank conflict, which measured cheaper than either reading 32
-  // bytes per lane pair without conflicts or selecting a per-lane row order
-  // that removes them.  Smaller panels: the k-group varies fastest.
+  // crowded the texture unit's address queue, so lane quads take
+  // consecutive mn-chunks and read 64 contiguous bytes: thread bits 0-1 are
+  // the chunk's low bits, the next 3 (256-row panels, 8 k-groups) or 4
+  // (128-row panels, 16 k-groups) bits the k-group, the rest the chunk's
+  // high bits.  The cost is on the LDS side: the 8 lanes of a write group
+  // land on fewer distinct swizzled chunks, a bank conflict, which measured
+  // cheaper than either reading 32 bytes per lane pair without conflicts or
+  // selecting a per-lane row order that removes them.  Other panel sizes:
+  // the k-group varies fastest.
   static_assert(KBN != 8 || NTH == 256, "the quad mapping covers 8 k-groups x 32 chunks");
   static __device__ __forceinline__ int kb_of(int tid) {
     if constexpr (KBN == 8) return (tid >> 2) & 7;
+    if constexpr (KBN == 16 && NTH == 256) return (tid >> 2) & 15;
     return tid % KBN;
   }
   static __device__ __forceinline__ int mc_of(int tid) {
     if constexpr (KBN == 8) return (tid & 3) | ((tid >> 5) << 2);
+    if constexpr (KBN == 16 && NTH == 256) return (tid & 3) | ((tid >> 6) << 2);
     return tid / KBN;
   }
   __device__ __forceinline__ void load(const uint16_t* __restrict__ X, int64_t ld, int r0,
