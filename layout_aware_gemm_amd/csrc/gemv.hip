@@ -11,9 +11,9 @@
 // K-vector v.  Two kernel shapes cover the two ways X can be stored:
 //   - rowdot: each row of X is K-contiguous (A 'N' for N = 1, B 'T' for
 //     M = 1): one wave per (row, K chunk), 16-byte loads of X and v.
-//   - colsweep: X is stored [K][L], L-contiguous (A 'T', B 'N'): a thread
-//     takes 8 consecutive outputs and walks a K chunk, the element v[k] is
-//     the same for the whole workgroup.
+//   - colsweep: X is stored [K][L], L-contiguous (A 'T', B 'N'): a
+//     workgroup takes 512 consecutive outputs (8 per lane) and splits a K
+//     chunk among its four waves; the element v[k] is the same for a wave.
 // Both write one fp32 partial per (K chunk, output) to the workspace;
 // combine then adds the chunks of each output in a fixed order -- so
 // results do not depend on scheduling -- and stores bf16 (round to nearest
@@ -89,8 +89,15 @@ __global__ void __launch_bounds__(256) rowdot_kernel(const uint16_t* __restrict_
   else store_out(C, (int64_t)r * sc, acc, out_f32);  // one chunk: no combine pass
 }
 
-// partial[kc * L + c] = sum over k in chunk kc of X[k*ldx + c] * v[k*sv] for
-// 8 consecutive c per thread.  VEC: ldx % 8 == 0 and X 16-byte aligned.
+// partial[kc * L + c] = sum over k in chunk kc of X[k*ldx + c] * v[k*sv].
+// A workgroup takes 512 consecutive c (8 per lane) and the chunk's rows in
+// four consecutive quarters, one per wave; the four wave sums are then
+// added in wave order through LDS.  Four waves per 512 outputs, rather than
+// one wave per 512 outputs and four times as many chunks, keep enough
+// loads in flight without four times the partials.  VEC: ldx % 8 == 0 and
+// X 16-byte aligned.
+constexpr int kSweepCols = 512;
+
 template <bool VEC>
 __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restrict__ X,
                                                        int64_t ldx, const uint16_t* __restrict__ v,
@@ -98,15 +105,20 @@ __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restric
                                                        int64_t kchunk, int nkc,
                                                        float* __restrict__ partial, void* C,
                                                        int64_t sc, int out_f32) {
-  const int c0 = (blockIdx.x * 256 + threadIdx.x) * 8;
+  __shared__ float red[4][kSweepCols];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c0 = blockIdx.x * kSweepCols + lane * 8;
   const int kc = blockIdx.y;
   const int64_t k0 = (int64_t)kc * kchunk;
   const int64_t k1 = k0 + kchunk < K ? k0 + kchunk : K;
+  const int64_t qr = (k1 - k0 + 3) / 4;  // rows per wave
+  const int64_t kw0 = k0 + wave * qr < k1 ? k0 + wave * qr : k1;
+  const int64_t kw1 = kw0 + qr < k1 ? kw0 + qr : k1;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
   if (c0 < L) {
     if (VEC && c0 + 8 <= L) {
-      int64_t k = k0;
-      for (; k + 4 <= k1; k += 4) {
+      int64_t k = kw0;
+      for (; k + 4 <= kw1; k += 4) {
         uint4 xr[4];
         float vk[4];
 #pragma unroll
@@ -124,7 +136,7 @@ __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restric
           }
         }
       }
-      for (; k < k1; ++k) {
+      for (; k < kw1; ++k) {
         const uint4 xr = *reinterpret_cast<const uint4*>(X + k * ldx + c0);
         const float vk = from_bf16(v[k * sv]);
         const uint32_t w[4] = {xr.x, xr.y, xr.z, xr.w};
@@ -135,19 +147,25 @@ __global__ void __launch_bounds__(256) colsweep_kernel(const uint16_t* __restric
         }
       }
     } else {
-      for (int64_t k = k0; k < k1; ++k) {
+      for (int64_t k = kw0; k < kw1; ++k) {
         const float vk = from_bf16(v[k * sv]);
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (c0 + e < L) acc[e] = fmaf(from_bf16(X[k * ldx + c0 + e]), vk, acc[e]);
       }
     }
+  }
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      if (c0 + e >= L) continue;
-      if (nkc > 1) partial[(int64_t)kc * L + c0 + e] = acc[e];
-      else store_out(C, (int64_t)(c0 + e) * sc, acc[e], out_f32);
-    }
+  for (int e = 0; e < 8; ++e) red[wave][lane * 8 + e] = acc[e];
+  __syncthreads();
+  if (wave != 0 || c0 >= L) return;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    if (c0 + e >= L) continue;
+    const int i = lane * 8 + e;
+    const float t = ((red[0][i] + red[1][i]) + red[2][i]) + red[3][i];
+    if (nkc > 1) partial[(int64_t)kc * L + c0 + e] = t;
+    else store_out(C, (int64_t)(c0 + e) * sc, t, out_f32);
   }
 }
 
@@ -233,9 +251,10 @@ int64_t gemv_chunks(int shape, int L, int64_t K) {
     if (n > most) n = most;
     return n < 1 ? 1 : n;
   }
-  // colsweep: at least ~1024 workgroups, chunks of at least 64 rows
-  const int64_t cb = cdiv(L, 2048);
-  int64_t n = cdiv(1024, cb);
+  // colsweep: at least ~2048 workgroups of 512 outputs, chunks of at least
+  // 64 rows (16 per wave)
+  const int64_t cb = cdiv(L, 512);
+  int64_t n = cdiv(2048, cb);
   const int64_t most = cdiv(K, 64);
   if (n > most) n = most;
   return n < 1 ? 1 : n;
@@ -262,7 +281,7 @@ hipError_t launch_gemv(int shape, const uint16_t* X, int64_t ldx, int64_t sx, co
     const int64_t kchunk = cdiv(K, nkc);
     nkc = (int)cdiv(K, kchunk);
     const bool vec = ldx % 8 == 0 && (reinterpret_cast<uintptr_t>(X) & 15) == 0;
-    const dim3 grid((unsigned)cdiv(L, 2048), (unsigned)nkc);
+    const dim3 grid((unsigned)cdiv(L, kSweepCols), (unsigned)nkc);
     if (vec)
       hipLaunchKernelGGL(colsweep_kernel<true>, grid, dim3(256), 0, s, X, ldx, v, sv, L, K, kchunk,
                          nkc, partial, C, sc, out_f32 ? 1 : 0);
