@@ -154,6 +154,19 @@ __device__ __forceinline__ void g_vec(uint4& v, float s, int rel) {
   v = make_uint4(w[0], w[1], w[2], w[3]);
 }
 
+// One dword (two elements) of a gradient vector without the label column:
+// each element only multiplied, with g_vec's bits (ce_grad_value without
+// the label is fma(e, s, 0)).
+__device__ __forceinline__ uint32_t g_dword_scale(uint32_t w, float s) {
+  return pack_bf16x2(__fmaf_rn(__uint_as_float(w << 16), s, 0.f),
+                     __fmaf_rn(__uint_as_float(w & 0xffff0000u), s, 0.f));
+}
+
+// Component d (0..3, a constant after unrolling) of a 16-byte vector.
+__device__ __forceinline__ uint32_t& u4ref(uint4& v, int d) {
+  return d == 0 ? v.x : (d == 1 ? v.y : (d == 2 ? v.z : v.w));
+}
+
 // ----------------------------------------------------------------------
 // Operand loaders.  R = rows of the panel (M or N extent of the tile).
 // ----------------------------------------------------------------------
@@ -223,14 +236,32 @@ struct LoaderKMajor {
     sstep = (uint32_t)(ld * (NTH / 8) * 2);
   }
 
-  __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    const __amdgpu_buffer_rsrc_t rs =
-        panel_rsrc(X + (int64_t)r0 * ld + k0, (uint32_t)(((int64_t)(R - 1) * ld + kBK) * 2));
+  __device__ __forceinline__ void load_interior(const uint16_t* X, int64_t ld, int r0, int k0,
+                                                bool zero = false) {
+    prep_interior(X, ld, r0, k0, zero);
 #pragma unroll
-    for (int i = 0; i < L; ++i) v[i] = buf_load16(rs, voff, i * sstep);
+    for (int i = 0; i < L; ++i) load_unit(i);
+  }
+
+  // The same loads one vector at a time (see LoaderMNMajor): zero
+  // (uniform) gives the buffer an empty range, so the vectors read as 0.
+#if defined(__HIP_DEVICE_COMPILE__)
+  __amdgpu_buffer_rsrc_t rs;
+#endif
+  __device__ __forceinline__ void prep_interior(const uint16_t* X, int64_t ld, int r0, int k0,
+                                                bool zero = false) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    rs = panel_rsrc(X + (int64_t)r0 * ld + k0,
+                    zero ? 0u : (uint32_t)(((int64_t)(R - 1) * ld + kBK) * 2));
 #else
-    (void)X, (void)ld, (void)r0, (void)k0;
+    (void)X, (void)ld, (void)r0, (void)k0, (void)zero;
+#endif
+  }
+  __device__ __forceinline__ void load_unit(int i) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    v[i] = buf_load16(rs, voff, i * sstep);
+#else
+    (void)i;
 #endif
   }
 
@@ -429,6 +460,25 @@ struct LoaderMNMajor {
     }
   }
 
+  // store_unit from the thread's unit-0 byte offset off0 (256-row panels):
+  // row mc*8 + i has the swizzle swz(mc*8) ^ (i/2), so unit i sits at byte
+  // (off0 ^ (i/2 << 4)) + 128 i -- one register for the eight units and an
+  // XOR each, where store_unit's addresses take four registers.
+  __device__ __forceinline__ uint32_t unit0_offset(int tid) const {
+    const int kb = kb_of(tid), mc = mc_of(tid);
+    return (uint32_t)((mc * 8 * kBK + ((kb ^ swz(mc * 8)) << 3)) * 2);
+  }
+  __device__ __forceinline__ void store_unit_at(uint16_t* lds, uint32_t off0, int i) const {
+    static_assert(L == 8, "256-row panels");
+    uint4 o;
+    o.x = pair(0, i);
+    o.y = pair(2, i);
+    o.z = pair(4, i);
+    o.w = pair(6, i);
+    *reinterpret_cast<uint4*>(reinterpret_cast<char*>(lds) + ((off0 ^ ((i >> 1) << 4)) + i * 128)) =
+        o;
+  }
+
   __device__ __forceinline__ void store(uint16_t* lds, int tid) const {
     const int kb = kb_of(tid), mc = mc_of(tid);
 #pragma unroll
@@ -575,6 +625,104 @@ struct DmaPanel {
                                         bool zero = false) const {
 #pragma unroll
     for (int j = 0; j < PER_WAVE; ++j) issue_one(origin, panel, wave_u, j, zero);
+  }
+};
+
+// ----------------------------------------------------------------------
+// Scales and labels of a cross-entropy gradient finished on load in the
+// two-set loop.  Each wave copies, straight into LDS words of its own, the
+// words its own lanes apply: per k-step one 256-byte direct copy of scales
+// (and, tokens along K, one of labels), issued just before the k-step's
+// register set, so the wait for that set covers them and no barrier is
+// needed.  The two register sets' words sit in two separate LDS arrays
+// (buf0, buf1), and AK's labels in a third: the compiler tells apart the
+// copies into distinct arrays, so a read of one set's words never waits
+// for the other set's copies still in flight.  Per wave and buffer: 64
+// scale words, then 64 label words.
+//  - AK (gradient read 'N': tokens along M, vocabulary along K): thread t's
+//    vectors are token rows t/8 + 32i; lane l of wave w stages row
+//    8w + l/8 + 32(l%8), so each thread's 8 rows are 8 consecutive words.
+//    A k-step is one 64-column chunk: one scale per row.  The rows'
+//    labels are staged once.
+//  - otherwise ('T': vocabulary along M, tokens along K): the lane-quad
+//    mapping puts all of wave w's vectors in the tile's 64-row chunk w, so
+//    the wave stages that chunk's scales of the k-step's 64 tokens and
+//    their labels, word l for token l.
+// ----------------------------------------------------------------------
+template <bool AK>
+struct GaStage {
+  static constexpr int kBufWords = 4 * 128;  // one buffer array: 4 waves
+  static constexpr int kLabWords = 4 * 64;   // AK's label array
+  static constexpr int kCopies = AK ? 1 : 2;  // copies per k-step (vector-memory operations)
+  uint32_t* area[2];  // this wave's words in buf0 / buf1 (wave-uniform)
+  uint32_t* labf;     // AK: this wave's labels
+  uint32_t voff;      // this lane's byte offset in a staged run
+
+  __device__ __forceinline__ void init(uint32_t* buf0, uint32_t* buf1, uint32_t* labs, int wave_u,
+                                       int lane) {
+    area[0] = buf0 + wave_u * 128;
+    area[1] = buf1 + wave_u * 128;
+    labf = labs + wave_u * 64;
+    voff = AK ? (uint32_t)((8 * wave_u + (lane >> 3) + 32 * (lane & 7)) * 4) : (uint32_t)(lane * 4);
+  }
+
+  // One 4-byte direct copy per lane from `origin` (wave-uniform) into `dst`;
+  // zero: an empty range, so the words read 0.
+  __device__ __forceinline__ void copy(const void* origin, uint32_t bytes, uint32_t* dst,
+                                       bool zero) const {
+#if defined(__HIP_DEVICE_COMPILE__)
+    const uint64_t base = reinterpret_cast<uint64_t>(origin);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)base);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(base >> 32));
+    void* src = reinterpret_cast<void*>(((uint64_t)hi << 32) | lo);
+    __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(src, (short)0, zero ? 0 : (int)bytes, 0x00020000);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 4,
+                                             (int)voff, 0, 0, 0);
+#else
+    (void)origin, (void)bytes, (void)dst, (void)zero;
+#endif
+  }
+
+  // The words of the k-step starting at column kg into buffer b.
+  __device__ __forceinline__ void issue(const GemmParams& p, int m0, int kg, int b, bool zero,
+                                        int wave_u) const {
+    if constexpr (AK) {
+      copy(p.gscale + (int64_t)(kg / kCeScaleCols) * p.gtok + m0, 256 * 4, area[b], zero);
+    } else {
+      copy(p.gscale + (int64_t)(m0 / kCeScaleCols + wave_u) * p.gtok + kg, 64 * 4, area[b],
+           zero);
+      copy(p.glabels + kg, 64 * 4, area[b] + 64, zero);
+    }
+  }
+  // AK: the labels of the tile's 256 token rows, once.
+  __device__ __forceinline__ void issue_labels(const GemmParams& p, int m0) const {
+    copy(p.glabels + m0, 256 * 4, labf, false);
+  }
+
+  // Staged words of buffer b (this thread's 8 are idx0 .. idx0+7): the
+  // labels, scales 2r and 2r+1, one label (a lane's own word idx = lane
+  // holds the token it staged).
+  __device__ __forceinline__ const uint32_t* lab_words(int b) const {
+    return AK ? labf : area[b] + 64;
+  }
+  __device__ __forceinline__ void read_labels(int b, int idx0, int (&lab)[8]) const {
+    const uint4* pl = reinterpret_cast<const uint4*>(lab_words(b) + idx0);
+    const uint4 l0 = pl[0], l1 = pl[1];
+    const uint32_t lw[8] = {l0.x, l0.y, l0.z, l0.w, l1.x, l1.y, l1.z, l1.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lab[i] = (int)lw[i];
+  }
+  __device__ __forceinline__ void read_scale_pair(int b, int idx0, int r, float (&s)[8]) const {
+    const uint2 q = *reinterpret_cast<const uint2*>(area[b] + idx0 + 2 * r);
+    s[2 * r] = __uint_as_float(q.x);
+    s[2 * r + 1] = __uint_as_float(q.y);
+  }
+  __device__ __forceinline__ int read_label(int b, int idx) const {
+    return (int)lab_words(b)[idx];
+  }
+  __device__ __forceinline__ float read_scale(int b, int idx) const {
+    return __uint_as_float(area[b][idx]);
   }
 };
 
@@ -1136,6 +1284,26 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, f32x16_t (&acc)[FM
 // One substep: MFMA q, one fragment read of the next substep (first FM+FN
 // slots, from pa / pb), and, when `cp` is set, this wave's copies of one
 // panel (d, origin o, into dst), spread evenly over the slots.
+// plain_substep with hook(q) run in slot q (side work spread between the
+// matrix-core instructions).
+template <int FM, int FN, bool SW, typename H>
+__device__ __forceinline__ void hook_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
+                                             const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
+                                             const uint16_t* rd_stage, int a_base, int b_base,
+                                             int xo, H&& hook) {
+  const uint16_t* pa = rd_stage + a_base + xo;
+  const uint16_t* pb = rd_stage + b_base + xo;
+#pragma unroll
+  for (int q = 0; q < FM * FN; ++q) {
+    const int i = q / FN, j = q % FN;
+    acc[i][j] = mma<SW>(fa[i], fb[j], acc[i][j]);
+    if (q < FM) na[q] = *reinterpret_cast<const bf16x8_t*>(pa + q * 32 * kBK);
+    else if (q < FM + FN) nb[q - FM] = *reinterpret_cast<const bf16x8_t*>(pb + (q - FM) * 32 * kBK);
+    hook(q);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 template <int FM, int FN, int R, bool SW>
 __device__ __forceinline__ void copy_substep(f32x16_t (&acc)[FM][FN], const bf16x8_t* fa,
                                              const bf16x8_t* fb, bf16x8_t* na, bf16x8_t* nb,
@@ -1391,21 +1559,58 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
 // stage during substep 2 of kt and, after the barrier, receive k-step
 // kt+3: seven substeps for their loads to arrive, where one set per operand
 // leaves three.
+// GA: A is a cross-entropy gradient finished on load (K-contiguous when AK,
+// so NN runs here too); its scales and labels come through GaStage, and
+// each A vector is transformed in substep 1 of the k-step that stores it,
+// one vector every other slot, before the stores of substep 2.
 // ----------------------------------------------------------------------
 // k-steps [k0/64, k0/64 + nk).
-template <int BM, int BN, int FM, int FN, bool SW>
+template <int BM, int BN, int FM, int FN, bool SW, bool AK = false, bool GA = false>
 __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n0, int k0, int nk,
-                                              uint16_t* lds, int tid, int a_base, int b_base,
-                                              const int* xo, f32x16_t (&acc)[FM][FN]) {
-  using LA = LoaderMNMajor<BM>;
+                                              uint16_t* __restrict__ lds,
+                                              uint32_t* __restrict__ gbuf0,
+                                              uint32_t* __restrict__ gbuf1,
+                                              uint32_t* __restrict__ glabs, int tid, int a_base,
+                                              int b_base, const int* xo,
+                                              f32x16_t (&acc)[FM][FN]) {
+  using LA = typename LoaderSel<AK, BM>::type;
   using LB = LoaderMNMajor<BN>;
-  constexpr int SA = BM * kBK, STAGE = (BM + BN) * kBK;
+  static_assert(!AK || GA, "K-contiguous A takes this loop only as a gradient");
+  static_assert(!GA || LA::L == 8, "the gradient transform covers 8 vectors per thread");
+  // LDS: stage s holds A at s*SSTR and B BOFF after it.  GA: A of stages
+  // 0 and 1, then B of stages 0 and 1, so that the two stages of a panel
+  // lie 32 KB apart, within the LDS instructions' immediate offset, and the
+  // LDS addresses of both stages share registers (the transform needs
+  // them; the plain loop measured 2% faster with the stages 64 KB apart).
+  static_assert(BM == BN, "one panel size");
+  constexpr int SA = BM * kBK;
+  constexpr int SSTR = GA ? SA : 2 * SA, BOFF = GA ? 2 * SA : SA;
+  const int bb = b_base - SA + BOFF;  // B's fragment rows, from the stage's A panel
   LA a0, a1;
   LB b0, b1;
   a0.init_interior(p.lda, tid);
   a1.init_interior(p.lda, tid);
   b0.init_interior(p.ldb, tid);
   b1.init_interior(p.ldb, tid);
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
+  GaStage<AK> ga;
+  // GA: this thread's first staged word, and what its label offsets are
+  // relative to (AK: the vector's first vocabulary column, less the
+  // k-step's; else the vector's first vocabulary row)
+  // (and, not AK, the first of the wave's 64 vocabulary rows)
+  int ga_idx0 = 0, ga_rel0 = 0, ga_hb = 0;
+  if constexpr (GA) {
+    ga.init(gbuf0, gbuf1, glabs, wave_u, tid & 63);
+    if constexpr (AK) {
+      ga.issue_labels(p, m0);
+      ga_idx0 = ((tid >> 3) & 7) * 8;
+      ga_rel0 = 8 * (tid & 7);
+    } else {
+      ga_idx0 = LA::kb_of(tid) * 8;
+      ga_rel0 = m0 + LA::mc_of(tid) * 8;
+      ga_hb = m0 + 64 * wave_u;
+    }
+  }
   // An even number of k-steps, nke, with k-step nk of zeros when nk is odd
   // (see mix_mainloop: one order of loads at the loop's entry and back
   // edge, so each set's stores wait for that set alone).  k-steps past nke
@@ -1413,43 +1618,145 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
   // alike.
   const int nke = nk + (nk & 1);
   auto kof = [nk](int t) { return (t < nk ? t : 0) * kBK; };
-  auto load = [&](LA& a, LB& b, int t) __attribute__((always_inline)) {
+  // (GA: the k-step's staged words first, so the wait for the set covers
+  // them; buffer = the set's index)
+  auto load = [&](LA& a, LB& b, int t, int buf) __attribute__((always_inline)) {
     const bool zero = t == nk && nke != nk;
+    if constexpr (GA) ga.issue(p, m0, k0 + kof(t), buf, zero, wave_u);
     a.load_interior(p.A, p.lda, m0, k0 + kof(t), zero);
     b.load_interior(p.B, p.ldb, n0, k0 + kof(t), zero);
   };
+  // GA: what the staged labels of k-step t are offset by
+  auto ga_rel = [&](int t) { return AK ? k0 + kof(t) + ga_rel0 : ga_rel0; };
+  // GA: whether any lane of the wave has a label column among its vectors
+  // of k-step t: each lane tests the label it staged against the wave's 64
+  // columns (AK) or rows
+  auto ga_hb_of = [&](int t) { return AK ? k0 + kof(t) : ga_hb; };
+  auto ga_wave_hit = [](int own, int hb) __attribute__((always_inline)) {
+    return __builtin_amdgcn_ballot_w64((unsigned)(own - hb) < 64u) != 0;
+  };
+  const uint32_t b_off0 = b0.unit0_offset(tid);
   // the sets for k-steps 0 / 2 and 1
-  load(a0, b0, 0);
-  load(a1, b1, 1);
+  load(a0, b0, 0, 0);
+  load(a1, b1, 1, 1);
+  if constexpr (GA) {
+    // (k-step 0's words: wait for their copies, before which only k-step
+    // 1's were issued -- and AK's labels, before k-step 0's)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(16 + GaStage<AK>::kCopies, 15));
+    float gsv[8];
+    int glv[8];
+    ga.read_labels(0, ga_idx0, glv);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ga.read_scale_pair(0, ga_idx0, r, gsv);
+    const int r0 = ga_rel(0);
+#pragma unroll
+    for (int v = 0; v < 8; ++v) g_vec(a0.v[v], gsv[v], glv[v] - r0);
+  }
   a0.store(lds, tid);
-  b0.store(lds + SA, tid);
-  load(a0, b0, 2);
+  b0.store(lds + BOFF, tid);
+  load(a0, b0, 2, 0);
   __syncthreads();
   bf16x8_t fa[2][FM], fb[2][FN];
-  read_frags<FM, FN>(lds, a_base, b_base, xo[0], fa[0], fb[0]);
+  read_frags<FM, FN>(lds, a_base, bb, xo[0], fa[0], fb[0]);
   // k-step kt; (a, b) hold k-step kt+1 and then receive kt+3
-  auto step = [&](LA& a, LB& b, int kt) __attribute__((always_inline)) {
+  auto step = [&](LA& a, LB& b, int kt, int buf) __attribute__((always_inline)) {
     const int cur = kt & 1;
-    const uint16_t* st = lds + cur * STAGE;
-    uint16_t* nx = lds + (cur ^ 1) * STAGE;
+    const uint16_t* st = lds + cur * SSTR;
+    uint16_t* nx = lds + (cur ^ 1) * SSTR;
     __builtin_amdgcn_sched_barrier(0);
-    plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[1]);
-    plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, b_base, xo[2]);
-    // (unconditional stores, as in mix_mainloop)
-    store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, b_base, xo[3], a, b,
-                               nx, nx + SA, tid, true);
+    if constexpr (GA) {
+      // The transform of set a (k-step kt+1), one dword of a vector (two
+      // elements, five vector instructions) per slot from slot 3 of
+      // substep 0 to slot 2 of substep 2, so that it issues in the shadow
+      // of the matrix-core instructions and without branches; substep 2
+      // then stores B's units first and A's last.  In a k-step where a
+      // lane of the wave has a label column among its vectors (about one
+      // in eight; each lane tests the label it staged against the wave's
+      // 64 columns (AK) or rows), slot 2 instead applies the full form to
+      // all eight vectors at once, and the spread dwords multiply by 1,
+      // which leaves bf16 values as they are.  Scales are read two at a
+      // time, two slots ahead, so few words are live.  The staged words
+      // are read only after an explicit wait for their copies: the
+      // vector-memory operations issued since are this set's 16 loads and
+      // k-step kt+2's copies and loads (the loop holds no other
+      // vector-memory operation; the vectors' own waits are the
+      // compiler's).
+      const int r0 = ga_rel(kt + 1);
+      float gsv[8];
+      int own = 0;
+      bool hit = false;
+      uint32_t bo = b_off0;
+      constexpr int SL = FM * FN, U = LA::U + LB::U;
+      auto slot = [&](int g) __attribute__((always_inline)) {
+        if (g == 0) {
+          __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 16 + GaStage<AK>::kCopies, 15));
+          own = ga.read_label(buf, tid & 63);
+        }
+        if (g % 8 == 1 && g < 32) {
+          const int r = g / 8;
+          ga.read_scale_pair(buf, ga_idx0, r, gsv);
+          if (r > 0 && hit) gsv[2 * r] = gsv[2 * r + 1] = 1.f;
+        }
+        if (g == 2) {
+          hit = ga_wave_hit(own, ga_hb_of(kt + 1));
+          if (hit) {
+            // (the empty asm keeps the reads inside this branch)
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int v = 0; v < 8; ++v)
+              g_vec(a.v[v], ga.read_scale(buf, ga_idx0 + v),
+                    ga.read_label(buf, ga_idx0 + v) - r0);
+            gsv[0] = gsv[1] = 1.f;
+          }
+        }
+        const int pc = g - 3;
+        if (pc >= 0 && pc < 32) {
+          const int v = pc >> 2, d = pc & 3;
+          uint32_t& w = u4ref(a.v[v], d);
+          w = g_dword_scale(w, gsv[v]);
+        }
+        if (g >= 2 * SL) {
+          // (unconditional stores, as in mix_mainloop)
+          const int q = g - 2 * SL;
+#pragma unroll
+          for (int u = (q * U + SL - 1) / SL; u < U && (u * SL) / U == q; ++u) {
+            if (u < LB::U)
+              b.store_unit_at(nx + BOFF, bo, u);
+            else
+              a.store_unit(nx, tid, u - LB::U);
+          }
+        }
+      };
+      hook_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, bb, xo[1],
+                               [&](int q) __attribute__((always_inline)) { slot(q); });
+      hook_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, bb, xo[2],
+                               [&](int q) __attribute__((always_inline)) { slot(SL + q); });
+      // B's units from one offset register that the empty asm makes opaque
+      // each step, so their addresses are made where they are used instead
+      // of held through the loop
+      asm volatile("" : "+v"(bo));
+      hook_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, bb, xo[3],
+                               [&](int q) __attribute__((always_inline)) { slot(2 * SL + q); });
+    } else {
+      plain_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, bb, xo[1]);
+      plain_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], st, a_base, bb, xo[2]);
+      // (unconditional stores, as in mix_mainloop)
+      store2_substep<FM, FN, SW>(acc, fa[0], fb[0], fa[1], fb[1], st, a_base, bb, xo[3], a, b,
+                                 nx, nx + BOFF, tid, true);
+    }
     __syncthreads();
     // the loads of k-step kt+3, spread over this substep
     const bool zero = kt + 3 == nk && nke != nk;
+    if constexpr (GA) ga.issue(p, m0, k0 + kof(kt + 3), buf, zero, wave_u);
     a.prep_interior(p.A, p.lda, m0, k0 + kof(kt + 3), zero);
     b.prep_interior(p.B, p.ldb, n0, k0 + kof(kt + 3), zero);
     // (in the last k-step this reads a stale stage that is never used)
-    load2_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, b_base, xo[0], a, b);
+    load2_substep<FM, FN, SW>(acc, fa[1], fb[1], fa[0], fb[0], nx, a_base, bb, xo[0], a, b);
   };
   // two unconditional steps per iteration (see mix_mainloop)
   for (int kt = 0; kt < nke; kt += 2) {
-    step(a1, b1, kt);
-    step(a0, b0, kt + 1);
+    step(a1, b1, kt, 1);
+    step(a0, b0, kt + 1, 0);
   }
   // the trailing loads must land before the registers are reused
   wait_dma();
@@ -1469,8 +1776,10 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr bool GA = EPI == kEpiGStoreBf16 || EPI == kEpiGStoreF32;  // CE gradient A on load
   // one K-contiguous operand, 256x256: the mixed loop (three D + two G panels)
   constexpr bool MIX = TGEMM_MIX && (A_KMAJOR != B_KMAJOR) && BM == 256 && BN == 256 && !Q8 && !GA;
-  // neither operand K-contiguous, 256x256: two register sets per operand
-  constexpr bool REG2 = TGEMM_MIX && !A_KMAJOR && !B_KMAJOR && BM == 256 && BN == 256 && !Q8 && !GA;
+  // neither operand K-contiguous, 256x256: two register sets per operand;
+  // also a gradient A (either layout) with B contiguous along N
+  constexpr bool REG2 = TGEMM_MIX && !B_KMAJOR && BM == 256 && BN == 256 && !Q8 &&
+                        (GA || !A_KMAJOR);
   // (NT: the three-buffer loop for 256- and 192-row tiles, the ring for 128)
   constexpr int DMA3 = 2 * SA + 3 * SB;
   constexpr int NT_LDS = BM == 128 ? (RING > 2 * STAGE ? RING : 2 * STAGE)
@@ -1478,6 +1787,12 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   constexpr int LDS_ELEMS =
       MIX ? DMA3 : ((A_KMAJOR && B_KMAJOR && !Q8 && !GA) ? NT_LDS : 2 * STAGE);
   __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  // the gradient's staged scales and labels (two-set loop): one array per
+  // register set, and the labels of K-contiguous gradient rows
+  __shared__ __attribute__((aligned(16))) uint32_t gbuf0[REG2 && GA ? GaStage<A_KMAJOR>::kBufWords : 4];
+  __shared__ __attribute__((aligned(16))) uint32_t gbuf1[REG2 && GA ? GaStage<A_KMAJOR>::kBufWords : 4];
+  __shared__ __attribute__((aligned(16)))
+  uint32_t glabs[REG2 && GA && A_KMAJOR ? GaStage<A_KMAJOR>::kLabWords : 4];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -1540,8 +1855,9 @@ __global__ void __launch_bounds__(kThreads, 1) gemm_kernel(GemmParams p) {
   }
   if constexpr (REG2) {
     if (interior) {
-      reg2_mainloop<BM, BN, FM, FN, SW>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds, tid, a_base,
-                                        b_base, xo, acc);
+      reg2_mainloop<BM, BN, FM, FN, SW, A_KMAJOR, GA>(p, m0, n0, kbeg, (kend - kbeg) / kBK, lds,
+                                                      gbuf0, gbuf1, glabs, tid, a_base, b_base,
+                                                      xo, acc);
       staged = true;
     }
   }

@@ -277,7 +277,11 @@ def test_ce_backward_oracle(M, V, K):
 
 @pytest.mark.parametrize("cfg", [0, 1, 2])
 @pytest.mark.parametrize("tb", ["N", "T"])
-@pytest.mark.parametrize("M,V,K,X", [(257, 520, 130, 200), (64, 256, 128, 96), (512, 768, 256, 384)])
+# (576, 832, 256, 320): odd k-step counts (13 for G . Y, 9 for G^T . Z) on
+# the 256x256 interior tiles, where a zero k-step pads the two-set loop,
+# and 64 x 64 blocks of which many hold a label column
+@pytest.mark.parametrize("M,V,K,X", [(257, 520, 130, 200), (64, 256, 128, 96), (512, 768, 256, 384),
+                                     (576, 832, 256, 320)])
 def test_ce_grad_on_load_equals_rescale_pass(M, V, K, X, tb, cfg):
     """Every layout and tile configuration of tgemm_run_ce_grad against
     tgemm_run on the finished gradient, bit for bit (bf16 and fp32 out);
