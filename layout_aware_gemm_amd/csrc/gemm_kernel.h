@@ -1687,17 +1687,23 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
       bool hit = false;
       uint32_t bo = b_off0;
       constexpr int SL = FM * FN, U = LA::U + LB::U;
+      // P0: the first dword's slot; RA: how many slots ahead of its first
+      // use a scale pair is read
+      constexpr int P0 = 3, RA = 2;
+      static_assert(P0 >= 3 && RA >= 1 && RA <= P0 && P0 + 31 < 2 * SL + LB::U,
+                    "the label test and the scale reads precede the dwords, which end "
+                    "before A's stores");
       auto slot = [&](int g) __attribute__((always_inline)) {
         if (g == 0) {
           __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 16 + GaStage<AK>::kCopies, 15));
           own = ga.read_label(buf, tid & 63);
         }
-        if (g % 8 == 1 && g < 32) {
-          const int r = g / 8;
+        if (g >= P0 - RA && (g - (P0 - RA)) % 8 == 0 && (g - (P0 - RA)) / 8 < 4) {
+          const int r = (g - (P0 - RA)) / 8;
           ga.read_scale_pair(buf, ga_idx0, r, gsv);
-          if (r > 0 && hit) gsv[2 * r] = gsv[2 * r + 1] = 1.f;
+          if (g > P0 - 1 && hit) gsv[2 * r] = gsv[2 * r + 1] = 1.f;
         }
-        if (g == 2) {
+        if (g == P0 - 1) {
           hit = ga_wave_hit(own, ga_hb_of(kt + 1));
           if (hit) {
             // (the empty asm keeps the reads inside this branch)
@@ -1709,7 +1715,7 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
             gsv[0] = gsv[1] = 1.f;
           }
         }
-        const int pc = g - 3;
+        const int pc = g - P0;
         if (pc >= 0 && pc < 32) {
           const int v = pc >> 2, d = pc & 3;
           uint32_t& w = u4ref(a.v[v], d);
