@@ -296,6 +296,26 @@ def rope_tables(steps, warmup):
     return out
 
 
+def mfma_ceiling(steps=20, warmup=40, iters=8192):
+    """The matrix-core ceiling (tgemm_mfma_ceiling): one workgroup per compute
+    unit, one wave per SIMD, 32x32x16 bf16 MFMAs on register operands only --
+    the GEMM loops' matrix-core work without loads, LDS or barriers.
+    ``warmup`` launches first, then ``steps`` timed ones; the clock probe
+    reads the clock at the end."""
+    import torch
+
+    from layout_aware_gemm_amd import tgemm
+
+    buf = torch.zeros(256 * 4, dtype=torch.float32, device="cuda")
+    probe = torch.zeros(3, dtype=torch.int64, device="cuda")
+    flop = 256 * 4 * iters * 524288.0
+    ms = time_stream(lambda i: tgemm.mfma_ceiling(iters, buf), steps, warmup, 1, probe=probe)
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"mfma_ceiling_32x32x16_tflops": round(tf, 1),
+            "mfma_ceiling_32x32x16_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
+            "mfma_ceiling_sclk_ghz_end": round(tgemm.clock_ghz(probe), 3)}
+
+
 def fp8_linear(K_, W_):
     """The float8 linear 4096x3072x4096 through tgemm_run_fp8 (cast passes
     plus the fp8 matrix-core GEMM), the weight read in place (NT) and from
@@ -365,6 +385,9 @@ def main():
     ap.add_argument("--only-fp8", action="store_true",
                     help="time only the fp8 linear 4096x3072x4096 (NT, NN) and the bf16 product "
                          "of its shape, and print the figures (a profiling command)")
+    ap.add_argument("--only-mfma-ceiling", action="store_true",
+                    help="time only the matrix-core ceiling kernel (32x32x16 bf16 MFMAs on "
+                         "register operands) and print the figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (the "
                          "reference kernel for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE; "
@@ -404,6 +427,9 @@ def main():
         return 0
     if args.only_fp8:
         print(json.dumps(fp8_linear(K_, W_)), flush=True)
+        return 0
+    if args.only_mfma_ceiling:
+        print(json.dumps(mfma_ceiling()), flush=True)
         return 0
     if args.only_sweep:
         log("timing the 4096^3 layout sweep ...")
@@ -521,6 +547,9 @@ def main():
 
         # ---- K=1 RoPE table --------------------------------------------------
         secondary.update(rope_tables(K_, W_))
+
+        # ---- matrix-core ceiling (no loads, LDS or barriers) -----------------
+        secondary.update(mfma_ceiling())
 
     traffic = measured_traffic()
     out = {

@@ -1,5 +1,7 @@
-// Shader-clock probe, a measurement aid beside the GEMM path.
+// Measurement aids beside the GEMM path: the shader-clock probe and the
+// matrix-core ceiling.
 //
+// Shader-clock probe.
 // MI355X lowers its shader clock under sustained matrix-core load, so a
 // kernel's rate at the clock it ran at can differ from its rate against the
 // nominal 2.4 GHz peak.  One wave reads the shader-cycle counter
@@ -32,8 +34,71 @@ __global__ void __launch_bounds__(64) clock_probe_kernel(uint64_t* out, uint64_t
   }
 }
 
+// Matrix-core ceiling.  Every wave issues nothing but MFMAs whose
+// operands sit in registers: per iteration, 16 independent 32x32
+// accumulator blocks each take one 32x32x16 bf16 MFMA (524288 flop per
+// wave), block q from operands a[q % 4] and b[q / 4], so no result feeds an
+// operand and no two blocks compute the same thing (the compiler would
+// merge them).  It is the GEMM loops' matrix-core work without loads, LDS
+// or barriers: the rate they could reach at the clock the chip holds under
+// such work.  Operands are finite bf16 values with random-looking bits
+// (sign, 7 mantissa bits, exponents 2^-7 .. 2^0) derived from the thread
+// and register index.  Lane 0 of each wave writes element 0 of block 0 to
+// out[block * 4 + wave].
+typedef __bf16 cl_bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float cl_f32x16_t __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ cl_bf16x8_t ceiling_operand(uint32_t seed) {
+  cl_bf16x8_t v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    uint32_t h = (seed + 0x9e3779b9u * (uint32_t)(e + 1)) * 0x85ebca6bu;
+    h ^= h >> 13;
+    // sign | exponent 120..127 | 7 mantissa bits
+    const uint16_t bits = (uint16_t)((h & 0x8000u) | ((120u + ((h >> 8) & 7u)) << 7) | (h & 0x7fu));
+    v[e] = __builtin_bit_cast(__bf16, bits);
+  }
+  return v;
+}
+
+__global__ void __launch_bounds__(256, 1) mfma_ceiling_kernel(int64_t iters, float* out) {
+  const uint32_t seed = (blockIdx.x * 256u + threadIdx.x) * 8u;
+  cl_bf16x8_t a[4], b[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    a[i] = ceiling_operand(seed + i);
+    b[i] = ceiling_operand(seed + 4 + i);
+  }
+  cl_f32x16_t acc[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[q][i] = 0.f;
+  for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q)
+      acc[q] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[q & 3], b[q >> 2], acc[q], 0, 0, 0);
+  }
+  float r = acc[0][0], keep = 0.f;
+#pragma unroll
+  for (int q = 1; q < 16; ++q) keep += acc[q][0];
+  // (every block feeds the result, so none is dropped)
+  if (keep == 12345.f) r += 1.f;
+  if ((threadIdx.x & 63u) == 0) out[blockIdx.x * 4 + (threadIdx.x >> 6)] = r;
+}
+
 }  // namespace
 }  // namespace tgemm
+
+extern "C" int tgemm_mfma_ceiling(int64_t iters, int blocks, float* out, void* stream) {
+  if (iters < 1 || iters > 100000000 || blocks < 1 || blocks > 65536 || out == nullptr ||
+      (reinterpret_cast<uintptr_t>(out) & 3) != 0)
+    return TGEMM_ERR_INVALID_ARG;
+  // (96 KB of LDS reserved, unused: one workgroup per compute unit)
+  hipLaunchKernelGGL(tgemm::mfma_ceiling_kernel, dim3(blocks), dim3(256), 96 * 1024,
+                     reinterpret_cast<hipStream_t>(stream), iters, out);
+  return hipGetLastError() == hipSuccess ? TGEMM_OK : TGEMM_ERR_HIP;
+}
 
 extern "C" int tgemm_clock_probe(int64_t ticks, uint64_t* out_ticks, void* stream) {
   if (ticks < 1 || ticks > 10000000 || out_ticks == nullptr ||

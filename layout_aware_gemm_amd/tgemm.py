@@ -35,7 +35,7 @@ EXPORTS = ("tgemm_run", "tgemm_run_fp8", "tgemm_validate", "tgemm_validate_fp8",
            "tgemm_set_fp8_cast_once", "tgemm_clock_probe", "tgemm_version",
            "tgemm_release_workspace", "tgemm_run_noalloc", "tgemm_noalloc_scratch_bytes",
            "tgemm_rope_region", "tgemm_validate_rope_region", "tgemm_run_ce_deferred",
-           "tgemm_run_ce_grad")
+           "tgemm_run_ce_grad", "tgemm_mfma_ceiling")
 
 
 class TgemmError(RuntimeError):
@@ -80,6 +80,8 @@ def lib():
         L.tgemm_set_fp8_cast_once.restype = ctypes.c_int
         L.tgemm_clock_probe.argtypes = [i64, vp, vp]
         L.tgemm_clock_probe.restype = ctypes.c_int
+        L.tgemm_mfma_ceiling.argtypes = [i64, ctypes.c_int, vp, vp]
+        L.tgemm_mfma_ceiling.restype = ctypes.c_int
         L.tgemm_version.argtypes = []
         L.tgemm_version.restype = ctypes.c_int
         L.tgemm_release_workspace.argtypes = [vp]
@@ -234,6 +236,19 @@ def clock_probe(ticks=2000, out=None, stream=None):
     r = lib().tgemm_clock_probe(int(ticks), _ptr(out), _stream(stream, out.device))
     if r != 0:
         raise TgemmError(r, "tgemm_clock_probe")
+    return out
+
+
+def mfma_ceiling(iters, out, blocks=256, stream=None):
+    """Enqueue the matrix-core ceiling kernel (``tgemm_mfma_ceiling``):
+    32x32x16 bf16 MFMAs on register operands, ``blocks * 4 * iters *
+    524288`` flop; ``out`` a CUDA float32 tensor of at least ``blocks * 4``
+    elements."""
+    if out.dtype != torch.float32 or out.numel() < blocks * 4 or not out.is_cuda:
+        raise ValueError("mfma_ceiling: out must be a CUDA float32 tensor of blocks * 4 elements")
+    r = lib().tgemm_mfma_ceiling(int(iters), int(blocks), _ptr(out), _stream(stream, out.device))
+    if r != 0:
+        raise TgemmError(r, "tgemm_mfma_ceiling")
     return out
 
 
