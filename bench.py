@@ -296,6 +296,49 @@ def rope_tables(steps, warmup):
     return out
 
 
+def torch_context(steps, warmup):
+    """Context only, not this library: the same products through torch (its
+    GEMM library) on the same inputs, and a plain fill of the RoPE table's
+    bytes.  NT 768x5120x13824 and 4096^3 NT as ``linear`` (X . W^T), the
+    gemv 1x5120x13824, the dot product of 10^8, a 537 MB fill."""
+    import torch
+    import torch.nn.functional as F
+
+    import workloads
+
+    dev = torch.device("cuda:0")
+    out = {}
+    w = workloads.nt_mlp()
+    X, W = w["X"].reshape(-1, 13824).to(dev), w["W"].to(dev)
+    ms = time_stream(lambda i: F.linear(X, W), steps, warmup, 1)
+    out["torch_nt_768x5120x13824_us"] = round(ms * 1e3, 2)
+    out["torch_nt_768x5120x13824_tflops"] = round(2.0 * 768 * 5120 * 13824 / (ms * 1e-3) / 1e12, 1)
+    x1 = X[:1].contiguous()
+    msg = time_stream(lambda i: F.linear(x1, W), steps, warmup, 1)
+    out["torch_gemv_1x5120x13824_us"] = round(msg * 1e3, 2)
+    del X, W, x1, w
+    ls = workloads.layout_sweep()
+    A, Bt = ls["opA"].to(dev), ls["opB"].t().contiguous().to(dev)
+    ms4 = time_stream(lambda i: F.linear(A, Bt), steps, warmup, 1)
+    out["torch_nt_4096_us"] = round(ms4 * 1e3, 2)
+    out["torch_nt_4096_tflops"] = round(2.0 * 4096 ** 3 / (ms4 * 1e-3) / 1e12, 1)
+    del A, Bt, ls
+    Kd = 10 ** 8
+    gdot = torch.Generator(device="cpu").manual_seed(5)
+    av = torch.randn(Kd, generator=gdot).to(torch.bfloat16).to(dev)
+    bv = torch.randn(Kd, generator=gdot).to(torch.bfloat16).to(dev)
+    msd = time_stream(lambda i: torch.dot(av, bv), steps, warmup, 1)
+    out["torch_dot_1e8_us"] = round(msd * 1e3, 2)
+    del av, bv
+    nbytes = 2 * 256 * 4096 * 128 * 2
+    buf = torch.empty(nbytes // 4, dtype=torch.float32, device=dev)
+    msf = time_stream(lambda i: buf.fill_(1.0), steps, warmup, 1)
+    out["fill_537MB_us"] = round(msf * 1e3, 2)
+    out["fill_537MB_frac_of_hbm"] = round(nbytes / (msf * 1e-3) / 1e9 / PEAK_HBM_GBS, 4)
+    del buf
+    return out
+
+
 def mfma_ceiling(steps=20, warmup=40, iters=8192):
     """The matrix-core ceiling (tgemm_mfma_ceiling): one workgroup per compute
     unit, one wave per SIMD, 32x32x16 bf16 MFMAs on register operands only --
@@ -385,6 +428,9 @@ def main():
     ap.add_argument("--only-fp8", action="store_true",
                     help="time only the fp8 linear 4096x3072x4096 (NT, NN) and the bf16 product "
                          "of its shape, and print the figures (a profiling command)")
+    ap.add_argument("--only-torch-context", action="store_true",
+                    help="time only torch's own kernels on the same products (context figures, "
+                         "not this library) and a plain fill, and print the figures")
     ap.add_argument("--only-mfma-ceiling", action="store_true",
                     help="time only the matrix-core ceiling kernel (32x32x16 bf16 MFMAs on "
                          "register operands) and print the figures")
@@ -430,6 +476,9 @@ def main():
         return 0
     if args.only_mfma_ceiling:
         print(json.dumps(mfma_ceiling()), flush=True)
+        return 0
+    if args.only_torch_context:
+        print(json.dumps(torch_context(K_, W_)), flush=True)
         return 0
     if args.only_sweep:
         log("timing the 4096^3 layout sweep ...")
