@@ -73,17 +73,21 @@ __device__ __forceinline__ uint32_t byte_col(uint32_t w0, uint32_t w1, uint32_t 
 
 // Operand stored contiguous along its rows' index: X [K][R] (row stride ld,
 // element (k, r) at X + k*ld + r).  A wave covers 8 chunks of 8 r by 8
-// groups of 16 k (lane = 8 * group + chunk): it reads 16 stored rows of
-// 128 contiguous bytes and writes 64 output rows of 128 contiguous bytes.
-// Each thread casts its 16 x 8 block and transposes the codes in registers.
+// groups of 16 k: it reads 16 stored rows of 128 contiguous bytes and
+// writes 64 output rows of 128 contiguous bytes.  Lane bits 0, 2 and 3 give
+// the chunk and bits 1, 4 and 5 the group, so lane pairs read 32
+// contiguous bytes and even/odd lane pairs write 32 contiguous bytes
+// (measured 1-2% faster on the fp8 linear NN than whole 128-byte runs on
+// one side only).  Each thread casts its 16 x 8 block and transposes the
+// codes in registers.
 __device__ __forceinline__ void pack_cols(const PackJob& j, int64_t gid) {
   const int lane = (int)(gid & 63);
   const int64_t wv = gid >> 6;
   const int kblocks = j.Kp >> 7;  // 128 k per wave
   const int64_t rb = wv / kblocks;
   const int kb = (int)(wv - rb * kblocks);
-  const int r0 = (int)(rb * 64) + 8 * (lane & 7);
-  const int k0 = kb * 128 + 16 * (lane >> 3);
+  const int r0 = (int)(rb * 64) + 8 * ((lane & 1) | ((lane >> 1) & 6));
+  const int k0 = kb * 128 + 16 * (((lane >> 1) & 1) | ((lane >> 3) & 6));
   const float s = j.scale[0];
   uint32_t lo[16], hi[16];  // codes of rows r0..r0+3 / r0+4..r0+7 at k0 + i
   const uint16_t* src = j.X + (int64_t)k0 * j.ld + r0;
