@@ -296,6 +296,47 @@ def rope_tables(steps, warmup):
     return out
 
 
+def ce_forward_backward(K_, W_):
+    """The fused CE GEMM (``fused_ce``), then the GEMMs that consume its
+    gradient, operands read as stored: dH = G . W (NN, K = 32000) and
+    dW = G^T . H (TN, K = 4096), on the finished gradient and with the
+    gradient finished on load (the fused CE without its rescale pass, the
+    scale table instead, then dH and dW reading the unscaled gradient)."""
+    import torch
+
+    from layout_aware_gemm_amd import tgemm
+
+    dev = torch.device("cuda:0")
+    Mc, Nc, Kc = 4096, 32000, 4096
+    out, Hs, Wv, g, lab_ce = fused_ce(max(5, K_ // 5), max(2, W_ // 5))
+    ce_fl = 2.0 * Mc * Nc * Kc
+    nst = max(5, K_ // 5)
+    dH = torch.empty(Mc, Kc, dtype=torch.bfloat16, device=dev)
+    dW = torch.empty(Nc, Kc, dtype=torch.bfloat16, device=dev)
+    ms_dh = time_stream(lambda i: tgemm.run("N", "N", Mc, Kc, Nc, g, Nc, Wv[0], Kc, dH, Kc,
+                                            tgemm.EPI_STORE_BF16), nst, 2, 1)
+    ms_dw = time_stream(lambda i: tgemm.run("T", "N", Nc, Kc, Mc, g, Nc, Hs[0], Kc, dW, Kc,
+                                            tgemm.EPI_STORE_BF16), nst, 2, 1)
+    out["ce_bwd_dH_NN_tflops"] = round(ce_fl / (ms_dh * 1e-3) / 1e12, 2)
+    out["ce_bwd_dW_TN_tflops"] = round(ce_fl / (ms_dw * 1e-3) / 1e12, 2)
+    lossd = torch.empty(Mc, dtype=torch.float32, device=dev)
+    sc = torch.empty((Nc + 63) // 64, Mc, dtype=torch.float32, device=dev)
+    ms_ced = time_stream(lambda i: tgemm.run_ce_deferred("N", "T", Mc, Nc, Kc, Hs[0], Kc, Wv[0],
+                                                         Kc, lab_ce, lossd, g, Nc, sc), nst, 2, 1)
+    ms_dh2 = time_stream(lambda i: tgemm.run_ce_grad("N", "N", Mc, Kc, Nc, g, Nc, sc, lab_ce,
+                                                     Wv[0], Kc, dH, Kc, tgemm.EPI_STORE_BF16),
+                         nst, 2, 1)
+    ms_dw2 = time_stream(lambda i: tgemm.run_ce_grad("T", "N", Nc, Kc, Mc, g, Nc, sc, lab_ce,
+                                                     Hs[0], Kc, dW, Kc, tgemm.EPI_STORE_BF16),
+                         nst, 2, 1)
+    out["ce_bwd_onload_dH_NN_tflops"] = round(ce_fl / (ms_dh2 * 1e-3) / 1e12, 2)
+    out["ce_bwd_onload_dW_TN_tflops"] = round(ce_fl / (ms_dw2 * 1e-3) / 1e12, 2)
+    out["ce_fwd_bwd_rescale_pass_route_us"] = round((out["ce_grad_ms"] + ms_dh + ms_dw) * 1e3, 1)
+    out["ce_fwd_bwd_on_load_route_us"] = round((ms_ced + ms_dh2 + ms_dw2) * 1e3, 1)
+    del Hs, Wv, g, dH, dW, sc, lossd
+    return out
+
+
 def torch_context(steps, warmup):
     """Context only, not this library: the same products through torch (its
     GEMM library) on the same inputs, and a plain fill of the RoPE table's
@@ -428,6 +469,9 @@ def main():
     ap.add_argument("--only-fp8", action="store_true",
                     help="time only the fp8 linear 4096x3072x4096 (NT, NN) and the bf16 product "
                          "of its shape, and print the figures (a profiling command)")
+    ap.add_argument("--only-ce-backward", action="store_true",
+                    help="time only the fused CE and the backward GEMMs on both gradient routes, "
+                         "and print the figures (a profiling command)")
     ap.add_argument("--only-torch-context", action="store_true",
                     help="time only torch's own kernels on the same products (context figures, "
                          "not this library) and a plain fill, and print the figures")
@@ -476,6 +520,9 @@ def main():
         return 0
     if args.only_mfma_ceiling:
         print(json.dumps(mfma_ceiling()), flush=True)
+        return 0
+    if args.only_ce_backward:
+        print(json.dumps(ce_forward_backward(K_, W_)), flush=True)
         return 0
     if args.only_torch_context:
         print(json.dumps(torch_context(K_, W_)), flush=True)
@@ -526,42 +573,8 @@ def main():
     del Xs, Ws, Ys, Xv
 
     if not args.only_nt:
-        # ---- fused cross-entropy GEMM ------------------------------------
-        Mc, Nc, Kc = 4096, 32000, 4096
-        ce_out, Hs, Wv, g, lab_ce = fused_ce(max(5, K_ // 5), max(2, W_ // 5))
-        secondary.update(ce_out)
-        ce_fl = 2.0 * Mc * Nc * Kc
-        # the GEMMs that consume the gradient, operands read as stored:
-        # dH = G . W (NN, K = 32000) and dW = G^T . H (TN, K = 4096)
-        dH = torch.empty(Mc, Kc, dtype=torch.bfloat16, device=dev)
-        dW = torch.empty(Nc, Kc, dtype=torch.bfloat16, device=dev)
-        ms_dh = time_stream(lambda i: tgemm.run("N", "N", Mc, Kc, Nc, g, Nc, Wv[0], Kc, dH, Kc,
-                                                tgemm.EPI_STORE_BF16), max(5, K_ // 5), 2, 1)
-        ms_dw = time_stream(lambda i: tgemm.run("T", "N", Nc, Kc, Mc, g, Nc, Hs[0], Kc, dW, Kc,
-                                                tgemm.EPI_STORE_BF16), max(5, K_ // 5), 2, 1)
-        secondary["ce_bwd_dH_NN_tflops"] = round(ce_fl / (ms_dh * 1e-3) / 1e12, 2)
-        secondary["ce_bwd_dW_TN_tflops"] = round(ce_fl / (ms_dw * 1e-3) / 1e12, 2)
-        # the same backward with the gradient finished on load: the fused CE
-        # without its rescale pass (the gradient's scale table instead), then
-        # dH and dW reading the unscaled gradient
-        nst = max(5, K_ // 5)
-        lossd = torch.empty(Mc, dtype=torch.float32, device=dev)
-        sc = torch.empty((Nc + 63) // 64, Mc, dtype=torch.float32, device=dev)
-        ms_ced = time_stream(lambda i: tgemm.run_ce_deferred("N", "T", Mc, Nc, Kc, Hs[0], Kc, Wv[0],
-                                                             Kc, lab_ce, lossd, g, Nc, sc),
-                             nst, 2, 1)
-        ms_dh2 = time_stream(lambda i: tgemm.run_ce_grad("N", "N", Mc, Kc, Nc, g, Nc, sc, lab_ce,
-                                                         Wv[0], Kc, dH, Kc, tgemm.EPI_STORE_BF16),
-                             nst, 2, 1)
-        ms_dw2 = time_stream(lambda i: tgemm.run_ce_grad("T", "N", Nc, Kc, Mc, g, Nc, sc, lab_ce,
-                                                         Hs[0], Kc, dW, Kc, tgemm.EPI_STORE_BF16),
-                             nst, 2, 1)
-        secondary["ce_bwd_onload_dH_NN_tflops"] = round(ce_fl / (ms_dh2 * 1e-3) / 1e12, 2)
-        secondary["ce_bwd_onload_dW_TN_tflops"] = round(ce_fl / (ms_dw2 * 1e-3) / 1e12, 2)
-        secondary["ce_fwd_bwd_rescale_pass_route_us"] = round(
-            (ce_out["ce_grad_ms"] + ms_dh + ms_dw) * 1e3, 1)
-        secondary["ce_fwd_bwd_on_load_route_us"] = round((ms_ced + ms_dh2 + ms_dw2) * 1e3, 1)
-        del Hs, Wv, g, dH, dW, sc, lossd
+        # ---- fused cross-entropy GEMM and the backward GEMMs ---------------
+        secondary.update(ce_forward_backward(K_, W_))
 
         # ---- layout sweep 4096^3 ------------------------------------------
         secondary.update(layout_sweep(K_, W_))
