@@ -1561,8 +1561,8 @@ __device__ __forceinline__ void mix_mainloop(const GemmParams& p, int m0, int n0
 // leaves three.
 // GA: A is a cross-entropy gradient finished on load (K-contiguous when AK,
 // so NN runs here too); its scales and labels come through GaStage, and
-// each A vector is transformed in substep 1 of the k-step that stores it,
-// one vector every other slot, before the stores of substep 2.
+// the A vectors are transformed one dword per slot over substeps 0 to 2 of
+// the k-step that stores them, before their LDS stores.
 // ----------------------------------------------------------------------
 // k-steps [k0/64, k0/64 + nk).
 template <int BM, int BN, int FM, int FN, bool SW, bool AK = false, bool GA = false>
@@ -1594,10 +1594,10 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
   b1.init_interior(p.ldb, tid);
   const int wave_u = __builtin_amdgcn_readfirstlane(tid >> 6);
   GaStage<AK> ga;
-  // GA: this thread's first staged word, and what its label offsets are
+  // GA: this thread's first staged word; what its label offsets are
   // relative to (AK: the vector's first vocabulary column, less the
-  // k-step's; else the vector's first vocabulary row)
-  // (and, not AK, the first of the wave's 64 vocabulary rows)
+  // k-step's; else the vector's first vocabulary row); not AK, the first of
+  // the wave's 64 vocabulary rows
   int ga_idx0 = 0, ga_rel0 = 0, ga_hb = 0;
   if constexpr (GA) {
     ga.init(gbuf0, gbuf1, glabs, wave_u, tid & 63);
@@ -1640,8 +1640,9 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
   load(a0, b0, 0, 0);
   load(a1, b1, 1, 1);
   if constexpr (GA) {
-    // (k-step 0's words: wait for their copies, before which only k-step
-    // 1's were issued -- and AK's labels, before k-step 0's)
+    // (k-step 0's words: wait until at most k-step 1's copies and loads
+    // are outstanding, so k-step 0's copies, and AK's labels issued before
+    // them, have landed)
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(16 + GaStage<AK>::kCopies, 15));
     float gsv[8];
     int glv[8];
@@ -1667,9 +1668,8 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
     if constexpr (GA) {
       // The transform of set a (k-step kt+1), one dword of a vector (two
       // elements, five vector instructions) per slot from slot 3 of
-      // substep 0 to slot 2 of substep 2, so that it issues in the shadow
-      // of the matrix-core instructions and without branches; substep 2
-      // then stores B's units first and A's last.  In a k-step where a
+      // substep 0 to slot 2 of substep 2, with no branch per vector;
+      // substep 2 then stores B's units first and A's last.  In a k-step where a
       // lane of the wave has a label column among its vectors (about one
       // in eight; each lane tests the label it staged against the wave's
       // 64 columns (AK) or rows), slot 2 instead applies the full form to
