@@ -1643,7 +1643,7 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
     // (k-step 0's words: wait until at most k-step 1's copies and loads
     // are outstanding, so k-step 0's copies, and AK's labels issued before
     // them, have landed)
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(16 + GaStage<AK>::kCopies, 15));
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(LA::L + LB::L + GaStage<AK>::kCopies, 15));
     float gsv[8];
     int glv[8];
     ga.read_labels(0, ga_idx0, glv);
@@ -1677,7 +1677,7 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
       // which leaves bf16 values as they are.  Scales are read two at a
       // time, two slots ahead, so few words are live.  The staged words
       // are read only after an explicit wait for their copies: the
-      // vector-memory operations issued since are this set's 16 loads and
+      // vector-memory operations issued since are this set's loads and
       // k-step kt+2's copies and loads (the loop holds no other
       // vector-memory operation; the vectors' own waits are the
       // compiler's).
@@ -1695,7 +1695,8 @@ __device__ __forceinline__ void reg2_mainloop(const GemmParams& p, int m0, int n
                     "before A's stores");
       auto slot = [&](int g) __attribute__((always_inline)) {
         if (g == 0) {
-          __builtin_amdgcn_s_waitcnt(waitcnt_imm(2 * 16 + GaStage<AK>::kCopies, 15));
+          __builtin_amdgcn_s_waitcnt(
+              waitcnt_imm(2 * (LA::L + LB::L) + GaStage<AK>::kCopies, 15));
           own = ga.read_label(buf, tid & 63);
         }
         if (g >= P0 - RA && (g - (P0 - RA)) % 8 == 0 && (g - (P0 - RA)) / 8 < 4) {
