@@ -19,7 +19,7 @@ namespace tgemm {
 namespace {
 
 constexpr int kPackThreads = 256;
-constexpr int kRowSeg = 1024;  // codes of one row per wave (rows kernel)
+constexpr int kRowSeg = 4096;  // codes of one row per wave (rows kernel): 8 loads per lane
 
 struct PackJob {
   const uint16_t* X;
@@ -33,29 +33,32 @@ struct PackJob {
 };
 
 // K-contiguous operand X [R][K] (row stride ld).  A wave takes a segment of
-// 1024 codes of one padded row: its two loads are 1 KB runs of the row
-// (lane l: elements 8l .. 8l+7 of each half), its two stores 512-byte runs
-// of the codes.  Elements at or past K, and rows at or past R, are code 0.
+// kRowSeg codes of one padded row: its loads are 1 KB runs of the row
+// (lane l: elements 8l .. 8l+7 of each 512-element part), all issued before
+// the first store, its stores 512-byte runs of the codes.  Eight loads in
+// flight per lane measured 5% faster on the fp8 linear NN than two.
+// Elements at or past K, and rows at or past R, are code 0.
 __device__ __forceinline__ void pack_rows(const PackJob& j, int64_t gid) {
   const int lane = (int)(gid & 63);
   const int64_t wv = gid >> 6;
   const int segs = (j.Kp + kRowSeg - 1) / kRowSeg;
   const int64_t r = wv / segs;
-  const int e0 = (int)(wv - r * segs) * kRowSeg + 8 * lane;  // first element, half 0
+  const int e0 = (int)(wv - r * segs) * kRowSeg + 8 * lane;  // first element, part 0
   const float s = j.scale[0];
   const uint16_t* row = j.X + r * j.ld;
   uint8_t* orow = j.out + r * j.Kp;
-  if (r < j.R && e0 + kRowSeg / 2 + 8 <= j.K) {
-    // the whole segment inside the operand (K % 8 == 0)
-    const uint4 v0 = *reinterpret_cast<const uint4*>(row + e0);
-    const uint4 v1 = *reinterpret_cast<const uint4*>(row + e0 + kRowSeg / 2);
-    *reinterpret_cast<uint2*>(orow + e0) = q8_codes(v0, s);
-    *reinterpret_cast<uint2*>(orow + e0 + kRowSeg / 2) = q8_codes(v1, s);
+  constexpr int NH = kRowSeg / 512;
+  if (r < j.R && e0 + (NH - 1) * 512 + 8 <= j.K) {
+    uint4 v[NH];
+#pragma unroll
+    for (int h = 0; h < NH; ++h) v[h] = *reinterpret_cast<const uint4*>(row + e0 + h * 512);
+#pragma unroll
+    for (int h = 0; h < NH; ++h) *reinterpret_cast<uint2*>(orow + e0 + h * 512) = q8_codes(v[h], s);
     return;
   }
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int e = e0 + h * (kRowSeg / 2);
+  for (int h = 0; h < NH; ++h) {
+    const int e = e0 + h * 512;
     if (e >= j.Kp) continue;  // (Kp % 128 == 0: a group of 8 is wholly inside or outside)
     uint2 c = make_uint2(0, 0);
     if (r < j.R && e < j.K) c = q8_codes(*reinterpret_cast<const uint4*>(row + e), s);
