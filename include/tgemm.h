@@ -159,7 +159,7 @@ TGEMM_API int tgemm_run(char transA, char transB, int64_t M, int64_t N, int64_t 
  * hipFree or other allocating call; the caller still owns every input and
  * output.  A call whose scratch need exceeds the array returns
  * TGEMM_ERR_WORKSPACE_LIMIT before anything is enqueued (the 768x5120x13824
- * NT product needs 60 MiB; split-K needs 4*chunks*M*N bytes, cross-entropy
+ * NT product needs 45 MiB: 3 K chunks; split-K needs 4*chunks*M*N bytes, cross-entropy
  * about 8*M*(N/128 + 1) bytes).
  *
  * Every call on a device shares that device's array, and the array keeps
