@@ -288,7 +288,12 @@ def test_ce_grad_on_load_equals_rescale_pass(M, V, K, X, tb, cfg):
     the gradient read as G and as G^T."""
     d = workloads.random_operands(M, V, K, "N", "T", seed=M + V + K, std=1.0)
     g = torch.Generator().manual_seed(X)
-    labels = torch.randint(0, V, (M,), generator=g, dtype=torch.int32).to(dev())
+    labels = torch.randint(0, V, (M,), generator=g, dtype=torch.int32)
+    # two rows whose labels fall outside [0, V): no one-hot term on either
+    # route (the losses are NaN, the gradients still defined)
+    labels[0] = -1
+    labels[M - 1] = V
+    labels = labels.to(dev())
     A, B = d["A"].to(dev()), d["B"].to(dev())
     loss, G = tgemm.cross_entropy(A, B.t(), labels, grad=True)
     _, E, S = tgemm.cross_entropy_deferred(A, B.t(), labels)
