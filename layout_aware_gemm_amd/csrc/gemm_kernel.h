@@ -633,12 +633,13 @@ struct DmaPanel {
 // two-set loop.  Each wave copies, straight into LDS words of its own, the
 // words its own lanes apply: per k-step one 256-byte direct copy of scales
 // (and, tokens along K, one of labels), issued just before the k-step's
-// register set, so the wait for that set covers them and no barrier is
-// needed.  The two register sets' words sit in two separate LDS arrays
-// (buf0, buf1), and AK's labels in a third: the compiler tells apart the
-// copies into distinct arrays, so a read of one set's words never waits
-// for the other set's copies still in flight.  Per wave and buffer: 64
-// scale words, then 64 label words.
+// register set, so no barrier is needed: the loop reads a set's words only
+// after an explicit wait for their copies (the compiler's own waits did not
+// cover them; a full-size run read stale words).  The two register sets'
+// words sit in two separate LDS arrays (buf0, buf1), and AK's labels in a
+// third: with one array, the compiler made every read of one set's words
+// wait for the other set's copies, issued a substep earlier.  Per wave and
+// buffer: 64 scale words, then 64 label words.
 //  - AK (gradient read 'N': tokens along M, vocabulary along K): thread t's
 //    vectors are token rows t/8 + 32i; lane l of wave w stages row
 //    8w + l/8 + 32(l%8), so each thread's 8 rows are 8 consecutive words.
