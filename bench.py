@@ -380,24 +380,29 @@ def torch_context(steps, warmup):
     return out
 
 
-def mfma_ceiling(steps=20, warmup=40, iters=8192):
+def mfma_ceiling(steps=20, warmup=40):
     """The matrix-core ceiling (tgemm_mfma_ceiling): one workgroup per compute
-    unit, one wave per SIMD, 32x32x16 bf16 MFMAs on register operands only --
-    the GEMM loops' matrix-core work without loads, LDS or barriers.
-    ``warmup`` launches first, then ``steps`` timed ones; the clock probe
-    reads the clock at the end."""
+    unit, one wave per SIMD, MFMAs on register operands only -- the GEMM
+    loops' matrix-core work without loads, LDS or barriers -- for bf16
+    (32x32x16) and fp8 (32x32x64).  ``warmup`` launches first, then ``steps``
+    timed ones; the clock probe reads the clock at the end."""
     import torch
 
     from layout_aware_gemm_amd import tgemm
 
     buf = torch.zeros(256 * 4, dtype=torch.float32, device="cuda")
     probe = torch.zeros(3, dtype=torch.int64, device="cuda")
-    flop = 256 * 4 * iters * 524288.0
-    ms = time_stream(lambda i: tgemm.mfma_ceiling(iters, buf), steps, warmup, 1, probe=probe)
-    tf = flop / (ms * 1e-3) / 1e12
-    return {"mfma_ceiling_32x32x16_tflops": round(tf, 1),
-            "mfma_ceiling_32x32x16_frac_of_peak": round(tf / PEAK_BF16_TFLOPS, 4),
-            "mfma_ceiling_sclk_ghz_end": round(tgemm.clock_ghz(probe), 3)}
+    out = {}
+    for kind, name, per, peak, iters in ((0, "32x32x16", 524288.0, PEAK_BF16_TFLOPS, 8192),
+                                         (1, "fp8_32x32x64", 2097152.0, PEAK_FP8_TFLOPS, 4096)):
+        flop = 256 * 4 * iters * per
+        ms = time_stream(lambda i: tgemm.mfma_ceiling(iters, buf, kind=kind), steps, warmup, 1,
+                         probe=probe)
+        tf = flop / (ms * 1e-3) / 1e12
+        out[f"mfma_ceiling_{name}_tflops"] = round(tf, 1)
+        out[f"mfma_ceiling_{name}_frac_of_peak"] = round(tf / peak, 4)
+        out[f"mfma_ceiling_{name}_sclk_ghz_end"] = round(tgemm.clock_ghz(probe), 3)
+    return out
 
 
 def fp8_linear(K_, W_):
@@ -476,7 +481,7 @@ def main():
                     help="time only torch's own kernels on the same products (context figures, "
                          "not this library) and a plain fill, and print the figures")
     ap.add_argument("--only-mfma-ceiling", action="store_true",
-                    help="time only the matrix-core ceiling kernel (32x32x16 bf16 MFMAs on "
+                    help="time only the matrix-core ceiling kernel (bf16 and fp8 MFMAs on "
                          "register operands) and print the figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a plain 1 GiB device-to-device copy, 5 times (the "

@@ -380,20 +380,21 @@ TGEMM_API int tgemm_clock_probe(int64_t ticks, uint64_t* out_ticks, void* stream
 /*
  * Matrix-core ceiling (a measurement aid, not part of the GEMM path):
  * enqueue `blocks` workgroups of 4 waves (one workgroup per compute unit,
- * one wave per SIMD) that each issue only v_mfma_f32_32x32x16_bf16 on
- * operands held in registers: `iters` iterations of 16 MFMAs into 16
- * independent accumulator blocks, 524288 flop per wave and iteration, from
- * finite bf16 operands.  The work is blocks * 4 * iters * 524288 flop;
- * timing it on `stream` gives the matrix-core rate without loads, LDS or
- * barriers at the clock the chip holds under it.  `out` (device,
- * float[blocks * 4], 4-byte aligned, caller-owned) receives element 0 of
- * block 0 of each wave, so the work is kept (iters = 2 gives twice the
- * values of iters = 1 up to the fp32 roundings of the accumulation).
- * Returns TGEMM_OK, TGEMM_ERR_INVALID_ARG (iters outside [1, 1e8], blocks
- * outside [1, 65536], NULL or misaligned out; checked before any device
- * call) or TGEMM_ERR_HIP.
+ * one wave per SIMD) that each issue only MFMAs on operands held in
+ * registers: `iters` iterations of 16 MFMAs into 16 independent 32x32
+ * accumulator blocks.  kind 0: v_mfma_f32_32x32x16_bf16 on finite bf16
+ * values, 524288 flop per wave and iteration; kind 1: the 32x32x64 MFMA on
+ * fp8 e4m3fn codes (never NaN), 2097152 flop.  The work is blocks * 4 *
+ * iters times that; timing it on `stream` gives the matrix-core rate
+ * without loads, LDS or barriers at the clock the chip holds under it.
+ * `out` (device, float[blocks * 4], 4-byte aligned, caller-owned) receives
+ * element 0 of block 0 of each wave, so the work is kept (iters = 2 gives
+ * twice the values of iters = 1 up to the fp32 roundings of the
+ * accumulation).  Returns TGEMM_OK, TGEMM_ERR_INVALID_ARG (kind not 0 or
+ * 1, iters outside [1, 1e8], blocks outside [1, 65536], NULL or misaligned
+ * out; checked before any device call) or TGEMM_ERR_HIP.
  */
-TGEMM_API int tgemm_mfma_ceiling(int64_t iters, int blocks, float* out, void* stream);
+TGEMM_API int tgemm_mfma_ceiling(int kind, int64_t iters, int blocks, float* out, void* stream);
 
 /*
  * Free the cached workspace buffer of (current device, `stream`) in stream

@@ -80,7 +80,7 @@ def lib():
         L.tgemm_set_fp8_cast_once.restype = ctypes.c_int
         L.tgemm_clock_probe.argtypes = [i64, vp, vp]
         L.tgemm_clock_probe.restype = ctypes.c_int
-        L.tgemm_mfma_ceiling.argtypes = [i64, ctypes.c_int, vp, vp]
+        L.tgemm_mfma_ceiling.argtypes = [ctypes.c_int, i64, ctypes.c_int, vp, vp]
         L.tgemm_mfma_ceiling.restype = ctypes.c_int
         L.tgemm_version.argtypes = []
         L.tgemm_version.restype = ctypes.c_int
@@ -239,14 +239,16 @@ def clock_probe(ticks=2000, out=None, stream=None):
     return out
 
 
-def mfma_ceiling(iters, out, blocks=256, stream=None):
-    """Enqueue the matrix-core ceiling kernel (``tgemm_mfma_ceiling``):
-    32x32x16 bf16 MFMAs on register operands, ``blocks * 4 * iters *
-    524288`` flop; ``out`` a CUDA float32 tensor of at least ``blocks * 4``
+def mfma_ceiling(iters, out, kind=0, blocks=256, stream=None):
+    """Enqueue the matrix-core ceiling kernel (``tgemm_mfma_ceiling``): MFMAs
+    on register operands, kind 0 = 32x32x16 bf16 (524288 flop per wave and
+    iteration), 1 = 32x32x64 fp8 e4m3fn (2097152); ``blocks * 4 * iters``
+    wave-iterations; ``out`` a CUDA float32 tensor of at least ``blocks * 4``
     elements."""
     if out.dtype != torch.float32 or out.numel() < blocks * 4 or not out.is_cuda:
         raise ValueError("mfma_ceiling: out must be a CUDA float32 tensor of blocks * 4 elements")
-    r = lib().tgemm_mfma_ceiling(int(iters), int(blocks), _ptr(out), _stream(stream, out.device))
+    r = lib().tgemm_mfma_ceiling(int(kind), int(iters), int(blocks), _ptr(out),
+                                 _stream(stream, out.device))
     if r != 0:
         raise TgemmError(r, "tgemm_mfma_ceiling")
     return out

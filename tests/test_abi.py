@@ -156,14 +156,15 @@ def test_clock_probe_rejects_before_touching_the_gpu():
 
 
 def test_mfma_ceiling_rejects_before_touching_the_gpu():
-    # iteration count, block count, NULL or misaligned output
+    # kind, iteration count, block count, NULL or misaligned output
     L = tgemm.lib()
-    assert L.tgemm_mfma_ceiling(0, 256, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
-    assert L.tgemm_mfma_ceiling(10 ** 8 + 1, 256, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
-    assert L.tgemm_mfma_ceiling(16, 0, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
-    assert L.tgemm_mfma_ceiling(16, 65537, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
-    assert L.tgemm_mfma_ceiling(16, 256, None, None) == tgemm.TGEMM_ERR_INVALID_ARG
-    assert L.tgemm_mfma_ceiling(16, 256, 18, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(2, 16, 256, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(0, 0, 256, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(1, 10 ** 8 + 1, 256, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(0, 16, 0, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(1, 16, 65537, 16, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(0, 16, 256, None, None) == tgemm.TGEMM_ERR_INVALID_ARG
+    assert L.tgemm_mfma_ceiling(1, 16, 256, 18, None) == tgemm.TGEMM_ERR_INVALID_ARG
 
 
 def test_set_fp8_cast_once_roundtrip():

@@ -30,15 +30,16 @@ def test_clock_probe_on_a_side_stream():
     assert 0.3 < tgemm.clock_ghz(out) < 3.5
 
 
-def test_mfma_ceiling_runs_and_keeps_its_work():
+@pytest.mark.parametrize("kind", [0, 1])
+def test_mfma_ceiling_runs_and_keeps_its_work(kind):
     # each accumulator block takes the same products every iteration, so two
     # iterations give twice one, up to the fp32 roundings of the matrix
     # core's accumulation (it does not add a whole product sum to the
     # accumulator in one rounding: not bit-exact); values finite, non-zero
     one = torch.zeros(256 * 4, dtype=torch.float32, device="cuda")
     two = torch.zeros_like(one)
-    tgemm.mfma_ceiling(1, one)
-    tgemm.mfma_ceiling(2, two)
+    tgemm.mfma_ceiling(1, one, kind=kind)
+    tgemm.mfma_ceiling(2, two, kind=kind)
     torch.cuda.synchronize()
     assert torch.isfinite(one).all() and torch.isfinite(two).all()
     assert (one != 0).all()
